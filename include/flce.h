@@ -1,0 +1,202 @@
+/*
+ * flce.h -- C ABI of the MI355X (gfx950) fused linear cross-entropy library.
+ *
+ * The operation (PR #1554 "skip ignore_index rows in the FLCE GEMMs", Summary;
+ * issue #1323 "Reduce FLCE weight-gradient allocation overhead across FP16,
+ * BF16, and FP32", Background and motivation):
+ *
+ *   for the labelled rows i (targets[i] != ignore_index):
+ *     z_i      = X[i,:] . W^T                       lm_head logits, never stored for all rows
+ *     loss_i   = logsumexp(z_i) - z_i[targets[i]]   cross-entropy
+ *     G_i      = s_i * (softmax(z_i) - onehot(targets[i]))
+ *     dX[i,:]  = G_i . W                            grad_input
+ *     dW      += G_i^T . X[i,:]                     grad_weight
+ *   with s_i = g / N (mean), g (sum) or g_i (none); g is the upstream
+ *   gradient, N the number of labelled rows.  Ignored rows get a zero dX row
+ *   and zero per-token loss and never enter a projection (PR #1554, Details
+ *   item 1 and Tests: NaN in ignored rows must not reach the loss or the
+ *   gradients).
+ *
+ * The rows are processed in chunks of chunk_size labelled rows; each chunk
+ * runs the logits projection into one reused [chunk_size, V] slab, the
+ * softmax-gradient pass in place, the grad_input projection and the
+ * grad_weight update written straight into dW (v0.8.3 commit bad6c3ec42,
+ * Summary: reusable logits, direct dX, direct dW; issue #1323, Proposed
+ * direction: no [V, H] temporary per chunk).  Loss and gradients are all
+ * produced by one forward call (PR #1554, Summary).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers to dense row-major arrays,
+ *     16-byte aligned, owned by the caller.  The library never allocates
+ *     device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All device work is enqueued on it, in order.
+ *   - Errors are returned as flce_status_t (0 = OK); nothing throws across
+ *     the ABI.  Argument, dtype and workspace errors are found on the host
+ *     before any launch and leave every output untouched.
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  X, W, dX and the slab use the operand dtype; dW uses the
+ * accumulation dtype, which is either the operand dtype or FLCE_F32
+ * (issue #1323, Proposed direction: same-dtype direct accumulation, and
+ * fp16/bf16 operands with an fp32 destination). */
+typedef enum { FLCE_F32 = 0, FLCE_F16 = 1, FLCE_BF16 = 2 } flce_dtype_t;
+
+/* Loss reductions (PR #1554, Tests: mean, sum and none with a per-token
+ * upstream gradient). */
+typedef enum { FLCE_MEAN = 0, FLCE_SUM = 1, FLCE_NONE = 2 } flce_reduction_t;
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_E_ARG = -1,       /* bad size, pointer, alignment or flag                */
+  FLCE_E_DTYPE = -2,     /* unsupported dtype / accumulation-dtype combination  */
+  FLCE_E_TARGET = -3,    /* a labelled target lies outside [0, V)               */
+  FLCE_E_WORKSPACE = -4, /* workspace smaller than flce_workspace_bytes()       */
+  FLCE_E_HIP = -5        /* HIP runtime error; see flce_last_error()            */
+} flce_status_t;
+
+/* Geometry and row counts of one flce_fwd_bwd call. */
+typedef struct {
+  int64_t chunk_size;   /* rows per chunk after flooring / clamping          */
+  int64_t chunks_total; /* ceil(BT / chunk_size): chunks with no row skipped */
+  int64_t chunks_run;   /* ceil(n_valid / chunk_size): chunks actually run   */
+  int64_t n_valid;      /* labelled rows                                      */
+  int32_t compacted;    /* 1 when skipping ignored rows removed a chunk       */
+  int32_t dx_splits;    /* split factor of the grad_input reduction over V    */
+} flce_stats_t;
+
+/*
+ * Rows per chunk.
+ *   chunk_size > 0 : floored to a power of two, then clamped to BT
+ *                    (PR #1439 "expose direct chunk-size control",
+ *                    Summary and Testing Done: 100 becomes 64).
+ *   chunk_size <= 0: heuristic from the memory constant C = chunk_mem_const
+ *                    (>= 1; v0.8.3 commit bad6c3ec42, Summary: public default
+ *                    C = 1, per-call override):
+ *                    next_pow2(ceil(BT / ceil(V / (C * H)))), clamped to BT.
+ *                    This form reproduces every geometry the pages print
+ *                    (PR #1439 review thread, C / num_chunks / chunk_size
+ *                    table; v0.8.3 commit, H200 memory and latency table).
+ * Returns the chunk size (>= 1), or FLCE_E_ARG for BT < 0, H < 1, V < 1,
+ * or chunk_size <= 0 with chunk_mem_const < 1.
+ */
+int64_t flce_chunk_size(int64_t BT, int64_t H, int64_t V, int64_t chunk_size,
+                        int32_t chunk_mem_const);
+
+/*
+ * Bytes of device workspace flce_fwd_bwd needs for these arguments.  The
+ * dominant term is the [chunk_size, V] logits slab in the operand dtype
+ * (chunk_size x V x itemsize, PR #1439, Summary), so with an explicit
+ * chunk_size it does not grow with BT except for 8 bytes per row of index
+ * and per-row loss.  Returns 0 for invalid arguments.
+ */
+size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,
+                            int64_t chunk_size, int32_t chunk_mem_const);
+
+/*
+ * Fused linear cross-entropy, forward and backward in one call.
+ *
+ *   X            [BT, H] dtype        inputs (rows = tokens)
+ *   W            [V, H]  dtype        lm_head weight
+ *   targets      [BT]    int64        class ids; rows equal to ignore_index are
+ *                                     ignored (any int64 value, default -100)
+ *   BT, H, V                          BT >= 0, H >= 8 and H % 8 == 0, V >= 1
+ *   dtype                             FLCE_F32, FLCE_F16 or FLCE_BF16
+ *   reduction                         FLCE_MEAN, FLCE_SUM or FLCE_NONE
+ *   chunk_size, chunk_mem_const       see flce_chunk_size
+ *   accum_dtype                       dtype of dW: FLCE_F32 or == dtype
+ *   frozen_weight                     1: no grad_weight work, dW may be NULL
+ *                                     (PR #1554, FLCE-alone tables: lm_head frozen)
+ *   accumulate_dw                     0: dW is overwritten; 1: dW += this call's gradient
+ *   grad_output  float, device        NULL means 1.  mean/sum: [1]; none: [BT].
+ *                                     Read only at labelled rows.
+ *   loss         float, device        mean/sum: [1]; none: [BT] with ignored rows +0.0.
+ *                                     Mean over zero labelled rows is 0.
+ *   dX           [BT, H] dtype        ignored rows +0.0
+ *   dW           [V, H] accum_dtype   see accumulate_dw
+ *   workspace    device, >= flce_workspace_bytes(...) bytes, 256-byte aligned
+ *   stream       hipStream_t as void*
+ *   stats        host pointer, may be NULL
+ *
+ * The call blocks once, on the host, after the row-compaction kernel, to read
+ * the labelled-row count and the target range check (PR #1554, Summary: one
+ * host sync).  Everything after that is enqueued asynchronously on `stream`;
+ * outputs are valid in stream order.  FLCE_E_TARGET is reported at that sync,
+ * before any projection runs; outputs are then unspecified.  Outputs must not
+ * alias inputs or the workspace.  Calls are reentrant given distinct
+ * workspaces.
+ */
+int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
+                 int64_t V, flce_dtype_t dtype, int64_t ignore_index, flce_reduction_t reduction,
+                 int64_t chunk_size, int32_t chunk_mem_const, flce_dtype_t accum_dtype,
+                 int32_t frozen_weight, int32_t accumulate_dw, const float* grad_output,
+                 float* loss, void* dX, void* dW, void* workspace, size_t workspace_bytes,
+                 void* stream, flce_stats_t* stats);
+
+/*
+ * dst[i] = scale * src[i], converted to dst_dtype (round to nearest even).
+ * Serves the wrapper's two elementwise steps: the final cast of an fp32
+ * grad_weight to the weight dtype (PR #1554, Tests: chunk storage is released
+ * before the final cast) and scaling the stored gradients by the upstream
+ * gradient in backward.  src [n] src_dtype, dst [n] dst_dtype, device
+ * pointers, 16-byte aligned; scale is a device float (NULL = 1).  src == dst
+ * is allowed when the dtypes match.  Enqueued on `stream`.
+ */
+int flce_scale_cast(const void* src, flce_dtype_t src_dtype, void* dst, flce_dtype_t dst_dtype,
+                    int64_t n, const float* scale, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* flce_status_string(int status);
+
+/* Detail of the last FLCE_E_HIP error raised on the calling thread. */
+const char* flce_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Measurement.  While a profile is open on the calling thread, every kernel
+ * that flce_fwd_bwd enqueues is bracketed by a pair of HIP events on the
+ * stream it runs on, and flce_profile_end sums their elapsed times per
+ * kernel kind.  This is how per-kernel durations are measured live for the
+ * roofline figures (the achieved rate of each kernel against MI355X peak).
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  FLCE_K_MASK_SCAN = 0,   /* ignore mask, prefix sum, labelled-row index, range check */
+  FLCE_K_ZERO_ROWS = 1,   /* zero dX / loss at ignored rows                          */
+  FLCE_K_LOGITS = 2,      /* logits GEMM into the slab (+ row max / sum-exp)         */
+  FLCE_K_SOFTMAX = 3,     /* in-place softmax-gradient pass over the slab            */
+  FLCE_K_DX = 4,          /* grad_input GEMM                                          */
+  FLCE_K_DX_REDUCE = 5,   /* fixed-order reduction of split grad_input partials      */
+  FLCE_K_DW = 6,          /* grad_weight GEMM written into dW                         */
+  FLCE_K_FINALIZE = 7,    /* loss reduction                                           */
+  FLCE_K_FILL = 8,        /* zero-fill / cast helpers                                 */
+  FLCE_K_COUNT = 9
+} flce_kernel_kind_t;
+
+typedef struct {
+  int64_t launches[FLCE_K_COUNT];
+  double total_ms[FLCE_K_COUNT];
+} flce_profile_t;
+
+/* Open a profile on the calling thread (clears any previous one). */
+int flce_profile_begin(void);
+
+/* Close it: waits for the recorded events and fills *out.  Returns
+ * FLCE_E_ARG if no profile is open. */
+int flce_profile_end(flce_profile_t* out);
+
+/* Name of a kernel kind (static storage). */
+const char* flce_kernel_name(int kind);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

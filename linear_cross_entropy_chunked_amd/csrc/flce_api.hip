@@ -1,0 +1,431 @@
+// Host side of the C ABI declared in include/flce.h: chunk policy, workspace
+// layout, argument checks, and the chunk loop that enqueues the kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "flce.h"
+#include "flce_internal.h"
+
+namespace {
+
+using namespace flce;
+
+// ------------------------------------------------------------ chunk policy
+int64_t floor_pow2(int64_t x) {
+  int64_t p = 1;
+  while (p <= x / 2) p <<= 1;
+  return p;
+}
+int64_t next_pow2(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+int64_t chunk_rows(int64_t BT, int64_t H, int64_t V, int64_t chunk_size, int32_t C) {
+  if (BT < 0 || H < 1 || V < 1) return FLCE_E_ARG;
+  int64_t c;
+  if (chunk_size > 0) {
+    // PR #1439: an explicit size is floored to a power of two and clamped to BT.
+    c = floor_pow2(chunk_size);
+  } else {
+    // v0.8.3 commit bad6c3ec42: memory budget of about C * BT * H elements
+    // for the [chunk, V] slab.  inc = ceil(V / (C * H)) chunks, each of
+    // next_pow2(ceil(BT / inc)) rows.
+    if (C < 1) return FLCE_E_ARG;
+    const int64_t inc = ceil_div(V, (int64_t)C * H);
+    c = next_pow2(ceil_div(BT, inc));
+  }
+  if (c > BT) c = BT;
+  if (c < 1) c = 1;
+  return c;
+}
+
+// ---------------------------------------------------------- workspace layout
+constexpr int64_t kAlign = 256;
+constexpr int kDxTargetBlocks = 512;     // aim for two workgroups per CU on 256 CUs
+constexpr int64_t kDxMinKPerSplit = 1024;
+constexpr int kDxMaxSplits = 32;
+
+struct Layout {
+  int64_t c = 0, ldz = 0, stats_ld = 0;
+  int splits = 1;
+  int64_t k_per_split = 0;
+  size_t off_slab = 0, off_stats = 0, off_ztgt = 0, off_partial = 0, off_idx = 0, off_lossrow = 0,
+         off_flags = 0, total = 0;
+};
+
+size_t itemsize(int dt) { return dt == FLCE_F32 ? 4 : 2; }
+
+Layout make_layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t c) {
+  Layout L;
+  L.c = c;
+  L.ldz = round_up(V, 8);
+  L.stats_ld = ceil_div(V, stats_cols_per_block());
+  const int64_t tiles = ceil_div(c, gemm_block_m()) * ceil_div(H, gemm_block_n());
+  int64_t splits = ceil_div(kDxTargetBlocks, tiles);
+  const int64_t by_k = L.ldz / kDxMinKPerSplit;
+  if (splits > by_k) splits = by_k;
+  if (splits > kDxMaxSplits) splits = kDxMaxSplits;
+  if (splits < 1) splits = 1;
+  L.k_per_split = round_up(ceil_div(L.ldz, splits), 64);
+  L.splits = (int)ceil_div(L.ldz, L.k_per_split);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (size_t)round_up((int64_t)bytes, kAlign);
+    return o;
+  };
+  L.off_slab = take((size_t)c * L.ldz * itemsize(dtype));
+  L.off_stats = take((size_t)c * L.stats_ld * 8);
+  L.off_ztgt = take((size_t)c * 4);
+  L.off_partial = take(L.splits > 1 ? (size_t)L.splits * c * H * 4 : 0);
+  L.off_idx = take((size_t)(BT > 0 ? BT : 1) * 4);
+  L.off_lossrow = take((size_t)(BT > 0 ? BT : 1) * 4);
+  L.off_flags = take(sizeof(ScanFlags));
+  L.total = off;
+  return L;
+}
+
+// ------------------------------------------------------------------ errors
+thread_local char g_last_error[512] = "";
+
+int fail_hip(hipError_t e, const char* what) {
+  std::snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what, hipGetErrorString(e),
+                (int)e);
+  return FLCE_E_HIP;
+}
+
+// --------------------------------------------------------------- profiling
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+struct Profiler {
+  bool open = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+thread_local Profiler g_prof;
+
+struct ProfScope {
+  hipStream_t st;
+  bool on = false;
+  ProfRec rec{};
+  ProfScope(int kind, hipStream_t s) : st(s) {
+    if (!g_prof.open) return;
+    rec.kind = kind;
+    rec.a = g_prof.get();
+    rec.b = g_prof.get();
+    if (rec.a && rec.b) {
+      on = true;
+      (void)hipEventRecord(rec.a, st);
+    }
+  }
+  ~ProfScope() {
+    if (!on) return;
+    (void)hipEventRecord(rec.b, st);
+    g_prof.recs.push_back(rec);
+  }
+};
+
+#define FLCE_LAUNCH(kind, expr)                       \
+  do {                                                \
+    hipError_t e_;                                    \
+    {                                                 \
+      ProfScope ps_(kind, st);                        \
+      e_ = (expr);                                    \
+    }                                                 \
+    if (e_ != hipSuccess) return fail_hip(e_, #expr); \
+  } while (0)
+
+// Pinned host word pair for the single device-to-host read.
+thread_local ScanFlags* g_host_flags = nullptr;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t flce_chunk_size(int64_t BT, int64_t H, int64_t V, int64_t chunk_size,
+                        int32_t chunk_mem_const) {
+  return chunk_rows(BT, H, V, chunk_size, chunk_mem_const);
+}
+
+size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,
+                            int64_t chunk_size, int32_t chunk_mem_const) {
+  if (dtype < FLCE_F32 || dtype > FLCE_BF16) return 0;
+  const int64_t c = chunk_rows(BT, H, V, chunk_size, chunk_mem_const);
+  if (c < 1) return 0;
+  return make_layout(BT, H, V, dtype, c).total;
+}
+
+const char* flce_status_string(int status) {
+  switch (status) {
+    case FLCE_OK: return "FLCE_OK";
+    case FLCE_E_ARG: return "FLCE_E_ARG: invalid argument";
+    case FLCE_E_DTYPE: return "FLCE_E_DTYPE: unsupported dtype combination";
+    case FLCE_E_TARGET: return "FLCE_E_TARGET: labelled target outside [0, V)";
+    case FLCE_E_WORKSPACE: return "FLCE_E_WORKSPACE: workspace too small";
+    case FLCE_E_HIP: return "FLCE_E_HIP: HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* flce_last_error(void) { return g_last_error; }
+
+const char* flce_kernel_name(int kind) {
+  static const char* names[FLCE_K_COUNT] = {"mask_scan",  "zero_ignored_rows", "logits_gemm",
+                                            "softmax_grad", "dx_gemm",         "dx_reduce",
+                                            "dw_gemm",    "loss_finalize",     "fill_cast"};
+  return (kind >= 0 && kind < FLCE_K_COUNT) ? names[kind] : "unknown";
+}
+
+int flce_profile_begin(void) {
+  for (auto& r : g_prof.recs) {
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  g_prof.open = true;
+  return FLCE_OK;
+}
+
+int flce_profile_end(flce_profile_t* out) {
+  if (!g_prof.open) return FLCE_E_ARG;
+  g_prof.open = false;
+  flce_profile_t p;
+  std::memset(&p, 0, sizeof p);
+  int rc = FLCE_OK;
+  for (auto& r : g_prof.recs) {
+    hipError_t e = hipEventSynchronize(r.b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) {
+      rc = fail_hip(e, "flce_profile_end");
+      continue;
+    }
+    p.launches[r.kind] += 1;
+    p.total_ms[r.kind] += ms;
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  if (out) *out = p;
+  return rc;
+}
+
+int flce_scale_cast(const void* src, flce_dtype_t src_dtype, void* dst, flce_dtype_t dst_dtype,
+                    int64_t n, const float* scale, void* stream) {
+  if (n < 0 || (n > 0 && (!src || !dst))) return FLCE_E_ARG;
+  if (src_dtype < FLCE_F32 || src_dtype > FLCE_BF16) return FLCE_E_DTYPE;
+  if (dst_dtype < FLCE_F32 || dst_dtype > FLCE_BF16) return FLCE_E_DTYPE;
+  if (src == dst && src_dtype != dst_dtype) return FLCE_E_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  FLCE_LAUNCH(FLCE_K_FILL, launch_scale_cast(src, (int)src_dtype, dst, (int)dst_dtype, n, scale,
+                                             st));
+  return FLCE_OK;
+}
+
+int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
+                 int64_t V, flce_dtype_t dtype, int64_t ignore_index, flce_reduction_t reduction,
+                 int64_t chunk_size, int32_t chunk_mem_const, flce_dtype_t accum_dtype,
+                 int32_t frozen_weight, int32_t accumulate_dw, const float* grad_output,
+                 float* loss, void* dX, void* dW, void* workspace, size_t workspace_bytes,
+                 void* stream, flce_stats_t* stats) {
+  // ---- host-side checks: nothing is launched or written on failure
+  if (dtype < FLCE_F32 || dtype > FLCE_BF16) return FLCE_E_DTYPE;
+  if (accum_dtype != dtype && accum_dtype != FLCE_F32) return FLCE_E_DTYPE;
+  if (reduction < FLCE_MEAN || reduction > FLCE_NONE) return FLCE_E_ARG;
+  if (BT < 0 || BT > 0x7ffffffe || V < 1 || V > 0x7ffffffe || H < 8 || H % 8 != 0 ||
+      H > 0x7ffffffe)
+    return FLCE_E_ARG;
+  if (frozen_weight != 0 && frozen_weight != 1) return FLCE_E_ARG;
+  if (accumulate_dw != 0 && accumulate_dw != 1) return FLCE_E_ARG;
+  if (!loss) return FLCE_E_ARG;
+  if (!frozen_weight && (!dW || !aligned(dW, 16))) return FLCE_E_ARG;
+  if (BT > 0 && (!X || !W || !targets || !dX)) return FLCE_E_ARG;
+  if (BT > 0 && (!aligned(X, 16) || !aligned(W, 16) || !aligned(dX, 16))) return FLCE_E_ARG;
+  const int64_t c = chunk_rows(BT, H, V, chunk_size, chunk_mem_const);
+  if (c < 1) return FLCE_E_ARG;
+  const Layout L = make_layout(BT, H, V, dtype, c);
+  if (!workspace || !aligned(workspace, kAlign)) return FLCE_E_ARG;
+  if (workspace_bytes < L.total) return FLCE_E_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int dt = (int)dtype;
+  const int red = (int)reduction;
+  const int dw_dt = (int)accum_dtype;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  void* slab = ws + L.off_slab;
+  float* stats_buf = reinterpret_cast<float*>(ws + L.off_stats);
+  float* ztgt = reinterpret_cast<float*>(ws + L.off_ztgt);
+  float* partial = reinterpret_cast<float*>(ws + L.off_partial);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + L.off_idx);
+  float* lossrow = reinterpret_cast<float*>(ws + L.off_lossrow);
+  ScanFlags* dflags = reinterpret_cast<ScanFlags*>(ws + L.off_flags);
+
+  if (stats) {
+    std::memset(stats, 0, sizeof *stats);
+    stats->chunk_size = c;
+    stats->chunks_total = ceil_div(BT, c);
+    stats->dx_splits = L.splits;
+  }
+
+  // ---- row compaction and the single host sync
+  int64_t N = 0;
+  if (BT > 0) {
+    FLCE_LAUNCH(FLCE_K_MASK_SCAN,
+                launch_mask_scan(targets, BT, V, ignore_index, idx, dflags, st));
+    FLCE_LAUNCH(FLCE_K_ZERO_ROWS,
+                launch_zero_ignored(targets, BT, H, ignore_index, dX, dt,
+                                    red == FLCE_NONE ? loss : nullptr, st));
+    if (!g_host_flags) {
+      hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&g_host_flags), 64,
+                                   hipHostMallocDefault);
+      if (e != hipSuccess) {
+        g_host_flags = nullptr;
+        return fail_hip(e, "hipHostMalloc");
+      }
+    }
+    hipError_t e = hipMemcpyAsync(g_host_flags, dflags, sizeof(ScanFlags), hipMemcpyDeviceToHost,
+                                  st);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(flags)");
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+    if (g_host_flags->bad_target) return FLCE_E_TARGET;
+    N = g_host_flags->n_valid;
+  }
+  const int64_t chunks = ceil_div(N, c);
+  if (stats) {
+    stats->n_valid = N;
+    stats->chunks_run = chunks;
+    stats->compacted = chunks < ceil_div(BT, c) ? 1 : 0;
+  }
+
+  if (!frozen_weight && !accumulate_dw && chunks == 0)
+    FLCE_LAUNCH(FLCE_K_FILL, launch_fill_zero(dW, V * H * (int64_t)itemsize(dw_dt), st));
+
+  const float inv_n = N > 0 ? 1.0f / (float)N : 0.f;
+  const int64_t stats_n = L.stats_ld;
+
+  // softmax pass geometry: enough workgroups to cover the chip, >= 2048 columns each
+  int parts = (int)ceil_div(2048, c);
+  const int64_t max_parts = ceil_div(L.ldz, 2048);
+  if (parts > max_parts) parts = (int)max_parts;
+  if (parts < 1) parts = 1;
+  const int64_t cols_per_part = round_up(ceil_div(L.ldz, parts), 8);
+
+  // ---- the chunk loop: logits -> softmax-gradient -> dX -> dW per chunk
+  for (int64_t k = 0; k < chunks; ++k) {
+    const int64_t base = k * c;
+    const int rows = (int)((N - base) < c ? (N - base) : c);
+    const int32_t* cidx = idx + base;
+
+    LogitsArgs la;
+    la.X = X;
+    la.W = W;
+    la.idx = cidx;
+    la.targets = targets;
+    la.rows = rows;
+    la.H = H;
+    la.V = V;
+    la.slab = slab;
+    la.ldz = L.ldz;
+    la.stats = stats_buf;
+    la.stats_ld = L.stats_ld;
+    la.ztgt = ztgt;
+    FLCE_LAUNCH(FLCE_K_LOGITS, launch_logits(dt, la, st));
+
+    SoftmaxArgs sa;
+    sa.slab = slab;
+    sa.ldz = L.ldz;
+    sa.V = V;
+    sa.rows = rows;
+    sa.stats = stats_buf;
+    sa.stats_ld = L.stats_ld;
+    sa.stats_n = stats_n;
+    sa.ztgt = ztgt;
+    sa.idx = cidx;
+    sa.targets = targets;
+    sa.grad_output = grad_output;
+    sa.reduction = red;
+    sa.lossrow = lossrow + base;
+    sa.loss_out = loss;
+    sa.parts = parts;
+    sa.cols_per_part = cols_per_part;
+    FLCE_LAUNCH(FLCE_K_SOFTMAX, launch_softmax(dt, sa, st));
+
+    DxArgs xa;
+    xa.slab = slab;
+    xa.W = W;
+    xa.idx = cidx;
+    xa.rows = rows;
+    xa.rows_cap = (int)c;
+    xa.H = H;
+    xa.V = V;
+    xa.ldz = L.ldz;
+    xa.splits = L.splits;
+    xa.k_per_split = L.k_per_split;
+    xa.dX = dX;
+    xa.partial = partial;
+    xa.grad_output = grad_output;
+    xa.inv_n = inv_n;
+    xa.reduction = red;
+    FLCE_LAUNCH(FLCE_K_DX, launch_dx(dt, xa, st));
+    if (L.splits > 1) {
+      DxReduceArgs ra;
+      ra.partial = partial;
+      ra.splits = L.splits;
+      ra.rows = rows;
+      ra.rows_cap = (int)c;
+      ra.H = H;
+      ra.idx = cidx;
+      ra.dX = dX;
+      ra.grad_output = grad_output;
+      ra.inv_n = inv_n;
+      ra.reduction = red;
+      FLCE_LAUNCH(FLCE_K_DX_REDUCE, launch_dx_reduce(dt, ra, st));
+    }
+
+    if (!frozen_weight) {
+      DwArgs wa;
+      wa.slab = slab;
+      wa.X = X;
+      wa.idx = cidx;
+      wa.rows = rows;
+      wa.H = H;
+      wa.V = V;
+      wa.ldz = L.ldz;
+      wa.dW = dW;
+      wa.dw_dtype = dw_dt;
+      wa.accumulate = (accumulate_dw || k > 0) ? 1 : 0;
+      wa.grad_output = grad_output;
+      wa.inv_n = inv_n;
+      wa.reduction = red;
+      FLCE_LAUNCH(FLCE_K_DW, launch_dw(dt, wa, st));
+    }
+  }
+
+  if (red != FLCE_NONE) FLCE_LAUNCH(FLCE_K_FINALIZE, launch_finalize(lossrow, (int)N,
+                                                                    red == FLCE_MEAN, loss, st));
+  return FLCE_OK;
+}
+
+}  // extern "C"

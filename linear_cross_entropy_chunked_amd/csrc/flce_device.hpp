@@ -1,0 +1,133 @@
+// Device-side building blocks for the gfx950 kernels: element types, exact
+// conversions, the MFMA tile step, wave reductions and the XCD-aware block
+// order.  Everything here is CDNA4 (wave64) specific.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flce {
+
+typedef unsigned short u16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_to_f32(u16 b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, IEEE round-to-nearest-even; NaN stays NaN.
+__device__ __forceinline__ u16 f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return u16((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u16(u >> 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(u16 h) {
+  _Float16 x = __builtin_bit_cast(_Float16, h);
+  return float(x);
+}
+
+__device__ __forceinline__ u16 f32_to_f16(float f) {
+  _Float16 x = _Float16(f);  // v_cvt_f16_f32, round-to-nearest-even
+  return __builtin_bit_cast(u16, x);
+}
+
+// ------------------------------------------------------------ element traits
+// 16-bit types: the 32x32x16 MFMA takes 8 consecutive k per lane (16 bytes).
+// fp32: the 32x32x2 MFMA takes 1 k per lane.
+struct BF16 {
+  typedef u16 storage;
+  static constexpr int kpack = 8;   // k per lane per MFMA
+  static constexpr int kstep = 16;  // k per MFMA
+  static constexpr int vec = 8;     // elements per 16-byte vector
+  __device__ static float to_f32(u16 x) { return bf16_to_f32(x); }
+  __device__ static u16 from_f32(float x) { return f32_to_bf16(x); }
+  __device__ static void mma(const u32x4_t& a, const u32x4_t& b, f32x16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+struct F16 {
+  typedef u16 storage;
+  static constexpr int kpack = 8;
+  static constexpr int kstep = 16;
+  static constexpr int vec = 8;
+  __device__ static float to_f32(u16 x) { return f16_to_f32(x); }
+  __device__ static u16 from_f32(float x) { return f32_to_f16(x); }
+  __device__ static void mma(const u32x4_t& a, const u32x4_t& b, f32x16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+struct F32 {
+  typedef float storage;
+  static constexpr int kpack = 1;
+  static constexpr int kstep = 2;
+  static constexpr int vec = 4;
+  __device__ static float to_f32(float x) { return x; }
+  __device__ static float from_f32(float x) { return x; }
+  __device__ static void mma(float a, float b, f32x16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Element store in a destination dtype chosen at run time (0 f32, 1 f16, 2 bf16).
+__device__ __forceinline__ void store_as(void* base, int64_t i, float v, int dt) {
+  if (dt == 0)
+    static_cast<float*>(base)[i] = v;
+  else if (dt == 1)
+    static_cast<u16*>(base)[i] = f32_to_f16(v);
+  else
+    static_cast<u16*>(base)[i] = f32_to_bf16(v);
+}
+
+__device__ __forceinline__ float load_as(const void* base, int64_t i, int dt) {
+  if (dt == 0) return static_cast<const float*>(base)[i];
+  if (dt == 1) return f16_to_f32(static_cast<const u16*>(base)[i]);
+  return bf16_to_f32(static_cast<const u16*>(base)[i]);
+}
+
+// ------------------------------------------------------------ wave reductions
+// Reductions over the 32 lanes of one half-wave (xor masks below 32 stay in
+// the half), used where the 32x32 MFMA tile spreads a row over 32 lanes.
+__device__ __forceinline__ float half_wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ __forceinline__ float half_wave_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// -------------------------------------------------------- XCD-aware ordering
+// Workgroups are handed to the 8 XCDs round-robin (hardware id i runs on XCD
+// i % 8).  This maps hardware ids to logical tile ids so that consecutive
+// logical ids run on one XCD and share its L2: XCD x receives the contiguous
+// logical range [x*q + min(x, r), ...), q = n / 8, r = n % 8.
+__device__ __forceinline__ int xcd_remap(int hw_id, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int x = hw_id & 7, j = hw_id >> 3;
+  return x * q + (x < r ? x : r) + j;
+}
+
+}  // namespace flce

@@ -1,0 +1,109 @@
+// Internal interface between the host orchestrator and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flce {
+
+// Logits GEMM of one chunk (rows = labelled rows in this chunk).
+struct LogitsArgs {
+  const void* X;           // [BT, H] operand dtype
+  const void* W;           // [V, H]
+  const int32_t* idx;      // [rows] labelled row ids of this chunk
+  const int64_t* targets;  // [BT]
+  int rows;
+  int64_t H, V;
+  void* slab;              // [rows_cap, ldz] operand dtype
+  int64_t ldz;
+  float* stats;            // [rows_cap, stats_ld] float2 (max, sum exp) per 64-column block
+  int64_t stats_ld;        // in float2 units
+  float* ztgt;             // [rows_cap] fp32 target logit
+};
+
+// Softmax-gradient pass of one chunk.
+struct SoftmaxArgs {
+  void* slab;
+  int64_t ldz, V;
+  int rows;
+  const float* stats;
+  int64_t stats_ld, stats_n;  // float2 row stride, live blocks per row
+  const float* ztgt;
+  const int32_t* idx;         // chunk's labelled row ids
+  const int64_t* targets;
+  const float* grad_output;   // none: [BT] per-row upstream gradient (NULL = 1)
+  int reduction;              // 0 mean, 1 sum, 2 none
+  float* lossrow;             // mean/sum: [rows] per-row loss of this chunk
+  float* loss_out;            // none: [BT] output
+  int parts;                  // workgroups per row
+  int64_t cols_per_part;      // multiple of 8
+};
+
+// grad_input GEMM of one chunk.
+struct DxArgs {
+  const void* slab;  // G [rows, ldz]
+  const void* W;     // [V, H]
+  const int32_t* idx;
+  int rows, rows_cap;
+  int64_t H, V, ldz;
+  int splits;
+  int64_t k_per_split;  // multiple of the GEMM k-tile
+  void* dX;             // [BT, H] (splits == 1)
+  float* partial;       // [splits, rows_cap, H] (splits > 1)
+  const float* grad_output;
+  float inv_n;
+  int reduction;
+};
+
+struct DxReduceArgs {
+  const float* partial;
+  int splits, rows, rows_cap;
+  int64_t H;
+  const int32_t* idx;
+  void* dX;
+  const float* grad_output;
+  float inv_n;
+  int reduction;
+};
+
+// grad_weight GEMM of one chunk.
+struct DwArgs {
+  const void* slab;  // G [rows, ldz]
+  const void* X;     // [BT, H]
+  const int32_t* idx;
+  int rows;
+  int64_t H, V, ldz;
+  void* dW;          // [V, H] dw_dtype
+  int dw_dtype;      // 0 f32, 1 f16, 2 bf16
+  int accumulate;    // 1: add to dW
+  const float* grad_output;
+  float inv_n;
+  int reduction;
+};
+
+// Device flags written by the mask/scan kernel and read by the host once.
+struct ScanFlags {
+  int32_t n_valid;
+  int32_t bad_target;
+};
+
+hipError_t launch_logits(int dtype, const LogitsArgs& a, hipStream_t st);
+hipError_t launch_dx(int dtype, const DxArgs& a, hipStream_t st);
+hipError_t launch_dw(int dtype, const DwArgs& a, hipStream_t st);
+hipError_t launch_softmax(int dtype, const SoftmaxArgs& a, hipStream_t st);
+hipError_t launch_dx_reduce(int dtype, const DxReduceArgs& a, hipStream_t st);
+hipError_t launch_mask_scan(const int64_t* targets, int64_t BT, int64_t V, int64_t ignore_index,
+                            int32_t* idx, ScanFlags* flags, hipStream_t st);
+hipError_t launch_zero_ignored(const int64_t* targets, int64_t BT, int64_t H,
+                               int64_t ignore_index, void* dX, int dx_dtype, float* loss_none,
+                               hipStream_t st);
+hipError_t launch_finalize(const float* lossrow, int n, int mean, float* loss, hipStream_t st);
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st);
+hipError_t launch_scale_cast(const void* src, int src_dtype, void* dst, int dst_dtype,
+                             int64_t n, const float* scale, hipStream_t st);
+
+int gemm_bk(int dtype);
+int stats_cols_per_block();
+int gemm_block_m();
+int gemm_block_n();
+
+}  // namespace flce

@@ -1,0 +1,318 @@
+// Bandwidth-bound kernels around the projections: ignored-row compaction,
+// zeroing of ignored outputs, the in-place softmax-gradient pass over the
+// logits slab, the fixed-order reduction of split grad_input partials, the
+// loss reduction, and fill / cast helpers.
+#include "flce_device.hpp"
+#include "flce_internal.h"
+
+namespace flce {
+
+// ---------------------------------------------------------------------------
+// Row compaction (PR #1554, Summary: the projections run only on rows whose
+// target is not ignore_index; nonzero() gives the row index and costs the one
+// host sync).  One workgroup: mask, exclusive prefix sum of the mask, and the
+// ascending list of labelled rows as int32; also flags labelled targets
+// outside [0, V).
+// ---------------------------------------------------------------------------
+constexpr int SCAN_T = 1024;
+constexpr int SCAN_PER = 8;
+
+__global__ __launch_bounds__(SCAN_T) void mask_scan_kernel(const int64_t* __restrict__ t,
+                                                           int64_t BT, int64_t V, int64_t ign,
+                                                           int32_t* __restrict__ idx,
+                                                           ScanFlags* flags) {
+  __shared__ int wave_tot[SCAN_T / kWave];
+  __shared__ int bad_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) bad_s = 0;
+  int base = 0;
+  int bad = 0;
+  for (int64_t s0 = 0; s0 < BT; s0 += (int64_t)SCAN_T * SCAN_PER) {
+    const int64_t e0 = s0 + (int64_t)tid * SCAN_PER;
+    unsigned mask = 0;
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < SCAN_PER; ++q) {
+      const int64_t e = e0 + q;
+      if (e < BT) {
+        const int64_t tv = t[e];
+        if (tv != ign) {
+          if (tv < 0 || tv >= V) bad = 1;
+          mask |= 1u << q;
+          ++cnt;
+        }
+      }
+    }
+    int x = cnt;  // inclusive scan within the wave
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int y = __shfl_up(x, d, kWave);
+      if (lane >= d) x += y;
+    }
+    if (lane == kWave - 1) wave_tot[wave] = x;
+    __syncthreads();
+    int wave_off = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < SCAN_T / kWave; ++w) {
+      const int c = wave_tot[w];
+      if (w < wave) wave_off += c;
+      total += c;
+    }
+    int pos = base + wave_off + x - cnt;
+#pragma unroll
+    for (int q = 0; q < SCAN_PER; ++q)
+      if (mask & (1u << q)) idx[pos++] = (int32_t)(e0 + q);
+    base += total;
+    __syncthreads();  // wave_tot is rewritten by the next tile
+  }
+  if (bad) atomicOr(&bad_s, 1);
+  __syncthreads();
+  if (tid == 0) {
+    flags->n_valid = base;
+    flags->bad_target = bad_s;
+  }
+}
+
+hipError_t launch_mask_scan(const int64_t* targets, int64_t BT, int64_t V, int64_t ignore_index,
+                            int32_t* idx, ScanFlags* flags, hipStream_t st) {
+  hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(SCAN_T), 0, st, targets, BT, V,
+                     ignore_index, idx, flags);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Ignored rows get a +0.0 grad_input row and +0.0 per-token loss (PR #1554,
+// Details item 1).  Labelled rows are left alone: the projections write them.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void zero_ignored_kernel(const int64_t* __restrict__ t,
+                                                           int64_t BT, int64_t row_vecs,
+                                                           int64_t ign, u32x4_t* dX,
+                                                           float* loss_none) {
+  for (int64_t row = blockIdx.x; row < BT; row += gridDim.x) {
+    if (t[row] != ign) continue;
+    u32x4_t* p = dX + row * row_vecs;
+    for (int64_t v = threadIdx.x; v < row_vecs; v += blockDim.x) p[v] = u32x4_t{0u, 0u, 0u, 0u};
+    if (loss_none && threadIdx.x == 0) loss_none[row] = 0.f;
+  }
+}
+
+hipError_t launch_zero_ignored(const int64_t* targets, int64_t BT, int64_t H,
+                               int64_t ignore_index, void* dX, int dx_dtype, float* loss_none,
+                               hipStream_t st) {
+  if (BT <= 0) return hipSuccess;
+  const int64_t row_bytes = H * (dx_dtype == 0 ? 4 : 2);
+  const int grid = (int)(BT < 2048 ? BT : 2048);
+  hipLaunchKernelGGL(zero_ignored_kernel, dim3(grid), dim3(256), 0, st, targets, BT,
+                     row_bytes / 16, ignore_index, static_cast<u32x4_t*>(dX), loss_none);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Softmax-gradient pass (v0.8.3 commit bad6c3ec42, Summary: the Triton fused
+// cross-entropy step; here one read and one write of the slab).  For row m of
+// the chunk:
+//   lse  = log sum_v exp(z_v), combined from the per-64-column (max, sum exp)
+//          pairs the logits GEMM left behind (fixed-order tree, fp32)
+//   loss = lse - z_t (z_t kept in fp32 by the logits GEMM)
+//   G_v  = gamma * (exp(z_v - lse) - [v == t]),  gamma = g_i for none, else 1
+// written over the logits in the operand dtype (round to nearest even); the
+// slab's padding columns [V, ldz) become 0.  The mean/sum scale g/N or g is
+// applied later, in fp32, by the gradient GEMMs: folding 1/N into a 16-bit
+// slab would flush small fp16 probabilities to zero.
+// ---------------------------------------------------------------------------
+constexpr int SM_T = 256;
+
+template <class T>
+__global__ __launch_bounds__(SM_T) void softmax_kernel(SoftmaxArgs a) {
+  typedef typename T::storage S;
+  __shared__ float red[SM_T / kWave];
+  __shared__ float bcast;
+  const int m = blockIdx.x / a.parts;
+  const int part = blockIdx.x % a.parts;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  const float2* st = reinterpret_cast<const float2*>(a.stats) + (int64_t)m * a.stats_ld;
+  float mx = -INFINITY;
+  for (int64_t j = tid; j < a.stats_n; j += SM_T) mx = fmaxf(mx, st[j].x);
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  if (tid == 0) {
+    float v = red[0];
+    for (int w = 1; w < SM_T / kWave; ++w) v = fmaxf(v, red[w]);
+    bcast = v;
+  }
+  __syncthreads();
+  const float M = bcast;
+  float s = 0.f;
+  for (int64_t j = tid; j < a.stats_n; j += SM_T) {
+    const float2 p = st[j];
+    s += p.y * __expf(p.x - M);
+  }
+  s = wave_sum(s);
+  __syncthreads();
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float v = red[0];
+    for (int w = 1; w < SM_T / kWave; ++w) v += red[w];
+    bcast = v;
+  }
+  __syncthreads();
+  const float lse = M + logf(bcast);
+
+  const int64_t row = a.idx[m];
+  const int64_t tgt = a.targets[row];
+  if (part == 0 && tid == 0) {
+    const float l = lse - a.ztgt[m];
+    if (a.reduction == 2)
+      a.loss_out[row] = l;
+    else
+      a.lossrow[m] = l;
+  }
+  const float gamma = (a.reduction == 2 && a.grad_output) ? a.grad_output[row] : 1.f;
+
+  S* z = static_cast<S*>(a.slab) + (int64_t)m * a.ldz;
+  const int64_t c_beg = (int64_t)part * a.cols_per_part;
+  int64_t c_end = c_beg + a.cols_per_part;
+  if (c_end > a.ldz) c_end = a.ldz;
+  constexpr int VE = T::vec;
+  for (int64_t c = c_beg + (int64_t)tid * VE; c < c_end; c += (int64_t)SM_T * VE) {
+    u32x4_t raw = *reinterpret_cast<const u32x4_t*>(z + c);
+    S* e = reinterpret_cast<S*>(&raw);
+#pragma unroll
+    for (int q = 0; q < VE; ++q) {
+      const int64_t col = c + q;
+      float g = 0.f;
+      if (col < a.V) {
+        const float p = __expf(T::to_f32(e[q]) - lse);
+        g = gamma * (col == tgt ? p - 1.f : p);
+      }
+      e[q] = T::from_f32(g);
+    }
+    *reinterpret_cast<u32x4_t*>(z + c) = raw;
+  }
+}
+
+hipError_t launch_softmax(int dtype, const SoftmaxArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.rows * a.parts));
+  if (dtype == 0)
+    hipLaunchKernelGGL(softmax_kernel<F32>, grid, dim3(SM_T), 0, st, a);
+  else if (dtype == 1)
+    hipLaunchKernelGGL(softmax_kernel<F16>, grid, dim3(SM_T), 0, st, a);
+  else
+    hipLaunchKernelGGL(softmax_kernel<BF16>, grid, dim3(SM_T), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split grad_input: dX[idx[m], n] = s * sum_split part[split][m][n], splits
+// summed in ascending order (deterministic), then scattered to the row.
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ __launch_bounds__(256) void dx_reduce_kernel(DxReduceArgs a) {
+  typedef typename T::storage S;
+  const int64_t total4 = (int64_t)a.rows * a.H / 4;
+  const float g = a.reduction == 2 ? 1.f : (a.grad_output ? a.grad_output[0] : 1.f);
+  const float s = a.reduction == 0 ? g * a.inv_n : g;
+  const int64_t plane = (int64_t)a.rows_cap * a.H;
+  S* dX = static_cast<S*>(a.dX);
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total4;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t f = e * 4;
+    const int64_t m = f / a.H, n = f % a.H;
+    f32x4_t acc = *reinterpret_cast<const f32x4_t*>(a.partial + f);
+    for (int sp = 1; sp < a.splits; ++sp) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.partial + sp * plane + f);
+      acc += v;
+    }
+    S* o = dX + (int64_t)a.idx[m] * a.H + n;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = T::from_f32(s * acc[q]);
+  }
+}
+
+hipError_t launch_dx_reduce(int dtype, const DxReduceArgs& a, hipStream_t st) {
+  const int64_t total4 = (int64_t)a.rows * a.H / 4;
+  int64_t blocks = (total4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  if (dtype == 0)
+    hipLaunchKernelGGL(dx_reduce_kernel<F32>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  else if (dtype == 1)
+    hipLaunchKernelGGL(dx_reduce_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(dx_reduce_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Loss reduction: sum of the per-row losses of the labelled rows, in a fixed
+// order (fp64 partial sums), divided by N for mean; 0 when N == 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void finalize_kernel(const float* __restrict__ lossrow, int n,
+                                                        int mean, float* loss) {
+  __shared__ double red[1024 / kWave];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  double s = 0.0;
+  for (int i = tid; i < n; i += 1024) s += (double)lossrow[i];
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) s += __shfl_xor(s, m, kWave);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  if (tid == 0) {
+    double v = 0.0;
+    for (int w = 0; w < 1024 / kWave; ++w) v += red[w];
+    if (mean) v = n > 0 ? v / (double)n : 0.0;
+    loss[0] = (float)v;
+  }
+}
+
+hipError_t launch_finalize(const float* lossrow, int n, int mean, float* loss, hipStream_t st) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, st, lossrow, n, mean, loss);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fill / cast helpers.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fill_zero_kernel(u32x4_t* p, int64_t nvec,
+                                                        unsigned char* tail, int tail_bytes) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = u32x4_t{0u, 0u, 0u, 0u};
+  if (blockIdx.x == 0 && (int)threadIdx.x < tail_bytes) tail[threadIdx.x] = 0;
+}
+
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st) {
+  if (bytes <= 0) return hipSuccess;
+  const int64_t nvec = bytes / 16;
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<u32x4_t*>(p), nvec,
+                     static_cast<unsigned char*>(p) + nvec * 16, (int)(bytes - nvec * 16));
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void scale_cast_kernel(const void* src, int sdt, void* dst,
+                                                         int ddt, int64_t n,
+                                                         const float* scale) {
+  const float s = scale ? scale[0] : 1.f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    store_as(dst, i, s * load_as(src, i, sdt), ddt);
+}
+
+hipError_t launch_scale_cast(const void* src, int src_dtype, void* dst, int dst_dtype,
+                             int64_t n, const float* scale, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(scale_cast_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, src_dtype,
+                     dst, dst_dtype, n, scale);
+  return hipGetLastError();
+}
+
+}  // namespace flce

@@ -1,0 +1,133 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no compute launched).
+
+* the library loads and exports every function include/flce.h declares;
+* the chunk policy reproduces every geometry the pages print;
+* workspace sizing follows the slab formula and is flat in BT for an
+  explicit chunk size;
+* invalid arguments are rejected on the host before any launch.
+"""
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "flce.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_exports_agree(flce_lib):
+    declared = _header_functions()
+    assert sorted(flce_lib.EXPORTS) == declared
+    lib = flce_lib.load()
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_exported_symbols_in_dynamic_table(flce_lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", flce_lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in _header_functions():
+        assert name in syms
+
+
+def test_status_and_kernel_names(flce_lib):
+    assert flce_lib.flce_status_string(0) == "FLCE_OK"
+    assert flce_lib.flce_status_string(-3).startswith("FLCE_E_TARGET")
+    assert [flce_lib.flce_kernel_name(k) for k in range(9)] == flce_lib.KERNEL_KINDS
+
+
+# ------------------------------------------------------------- chunk policy
+def test_heuristic_geometry_matches_pages(flce_lib):
+    geo = json.load(open(os.path.join(GOLDEN, "chunk_geometry.json")))
+    for g in geo["heuristic"]:
+        c = flce_lib.flce_chunk_size(g["BT"], g["H"], g["V"], 0, g["C"])
+        assert c == g["chunk_size"], g
+        assert -(-g["BT"] // c) == g["num_chunks"], g
+
+
+def test_slab_bytes_match_pages(flce_lib):
+    geo = json.load(open(os.path.join(GOLDEN, "chunk_geometry.json")))
+    for g in geo["slab_bytes"]:
+        c = flce_lib.flce_chunk_size(g["BT"], g["H"], g["V"], 0, g["C"])
+        assert c * g["V"] * g["itemsize"] == g["bytes"]
+
+
+def test_explicit_chunk_size_floor_and_clamp(flce_lib):
+    geo = json.load(open(os.path.join(GOLDEN, "chunk_geometry.json")))
+    for g in geo["explicit"]:
+        assert flce_lib.flce_chunk_size(g["BT"], 4096, 128256, g["requested"], 1) == g["chunk_size"]
+    assert flce_lib.flce_chunk_size(300, 128, 1000, 512, 1) == 300   # clamp to BT
+    assert flce_lib.flce_chunk_size(300, 128, 1000, 1, 1) == 1
+    assert flce_lib.flce_chunk_size(0, 128, 1000, 64, 1) == 1         # empty batch
+    assert flce_lib.flce_chunk_size(300, 128, 1000, 0, 0) == -1        # C must be >= 1
+    assert flce_lib.flce_chunk_size(300, 0, 1000, 64, 1) == -1
+    assert flce_lib.flce_chunk_size(-1, 128, 1000, 64, 1) == -1
+
+
+def test_skip_whole_chunks_geometry(flce_lib):
+    """40 rows at chunk 16: 0/1/8/24/40 ignored -> 3/3/2/1/0 logits GEMMs (count = ceil(N/c))."""
+    g = json.load(open(os.path.join(GOLDEN, "chunk_geometry.json")))["skip_whole_chunks"]
+    c = flce_lib.flce_chunk_size(g["BT"], 64, 100, g["chunk_size"], 1)
+    assert c == 16
+    for ign, gemms in zip(g["ignored"], g["logits_gemms"]):
+        assert -(-(g["BT"] - ign) // c) == gemms
+
+
+def test_workspace_flat_in_bt_for_explicit_chunk(flce_lib):
+    H, V = 5376, 262144
+    a = flce_lib.flce_workspace_bytes(8192, H, V, flce_lib.BF16, 256, 1)
+    b = flce_lib.flce_workspace_bytes(32768, H, V, flce_lib.BF16, 256, 1)
+    slab = 256 * V * 2
+    assert a >= slab and b >= slab
+    # only the 8 bytes per row of index and per-row loss grow with BT
+    assert b - a <= 8 * (32768 - 8192) + 4 * 256
+    # the heuristic's slab grows with BT (chunk 256 -> 1024)
+    h8 = flce_lib.flce_workspace_bytes(8192, H, V, flce_lib.BF16, 0, 1)
+    h32 = flce_lib.flce_workspace_bytes(32768, H, V, flce_lib.BF16, 0, 1)
+    assert h32 - h8 >= (1024 - 256) * V * 2
+
+
+def test_workspace_invalid_arguments(flce_lib):
+    assert flce_lib.flce_workspace_bytes(128, 64, 100, 7, 64, 1) == 0
+    assert flce_lib.flce_workspace_bytes(128, 0, 100, 0, 64, 1) == 0
+
+
+# ------------------------------------------------ rejected before any launch
+def _call(flce_lib, **kw):
+    a = dict(X=16, W=16, targets=16, BT=4, H=64, V=10, dtype=flce_lib.BF16, ignore_index=-100,
+             reduction=0, chunk_size=0, chunk_mem_const=1, accum_dtype=flce_lib.BF16,
+             frozen_weight=0, accumulate_dw=0, grad_output=None, loss=16, dX=16, dW=16,
+             workspace=256, workspace_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return flce_lib.flce_fwd_bwd(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), -2),
+    (dict(accum_dtype=1), -2),                 # bf16 operands, fp16 dW
+    (dict(reduction=3), -1),
+    (dict(H=60), -1),                          # H must be a multiple of 8
+    (dict(H=0), -1),
+    (dict(V=0), -1),
+    (dict(BT=-1), -1),
+    (dict(loss=None), -1),
+    (dict(dW=None), -1),                       # trained weight needs dW
+    (dict(X=None), -1),
+    (dict(X=18), -1),                          # misaligned
+    (dict(workspace=None), -1),
+    (dict(workspace=272), -1),                 # workspace must be 256-byte aligned
+    (dict(workspace_bytes=1), -4),
+    (dict(chunk_mem_const=0), -1),
+    (dict(frozen_weight=2), -1),
+])
+def test_invalid_arguments_rejected_on_host(flce_lib, kw, status):
+    assert _call(flce_lib, **kw) == status

@@ -1,0 +1,260 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Element-by-element comparison (relative Frobenius error) on the same seeded
+inputs, at sizes the oracle finishes in seconds that still span several
+GEMM tiles, several chunks and a ragged last chunk.  Tolerances: fp32 loss
+1e-5 and gradients 1e-4; bf16/fp16 loss 2e-3 and gradients 2e-2.  The
+labelled-row count, the chunk counts and every ignored-row output are exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-3, 2e-2), "f16": (2e-3, 2e-2)}
+TD = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@pytest.fixture(scope="module")
+def pkg(flce_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return flce_lib
+
+
+def _rel(gpu, ref):
+    a = gpu.detach().double().cpu().numpy() if hasattr(gpu, "detach") else np.asarray(gpu)
+    b = np.asarray(ref, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def _run(pkg, X, W, t, **kw):
+    dev = torch.device("cuda:0")
+    g = kw.pop("grad_output", None)
+    dW0 = kw.pop("dW_init", None)
+    if dW0 is not None:
+        kw["dW"] = dW0.clone().to(dev)
+        kw["accumulate_dw"] = True
+    r = pkg.fused_linear_cross_entropy_fwd_bwd(
+        X.to(dev), W.to(dev), t.to(dev), grad_output=None if g is None else g.to(dev), **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def _check(r, ref, dtype, reduction, frozen=False):
+    tl, tg = TOL[dtype]
+    if reduction == "none":
+        assert _rel(r.loss, ref["loss"]) <= tl
+    else:
+        lo = float(r.loss)
+        assert abs(lo - ref["loss"]) <= tl * max(abs(ref["loss"]), 1e-30), (lo, ref["loss"])
+    assert _rel(r.dX, ref["dX"]) <= tg, _rel(r.dX, ref["dX"])
+    if not frozen:
+        assert _rel(r.dW, ref["dW"]) <= tg, _rel(r.dW, ref["dW"])
+
+
+# ------------------------------------------------------------- the tiny workload
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+@pytest.mark.parametrize("chunk", [16, 64, 256])
+def test_tiny_fp32(pkg, reduction, chunk):
+    cfg = si.WORKLOADS["tiny"]
+    X, W, t = si.make_case(cfg["BT"], cfg["H"], cfg["V"], "f32", cfg["seed"], ignore="scattered",
+                           frac=cfg["frac"])
+    g = si.make_grad_output(t, reduction, cfg["seed"], scalar=0.75)
+    r = _run(pkg, X, W, t, reduction=reduction, chunk_size=chunk, accum_dtype=torch.float32,
+             grad_output=g)
+    ref = oracle.flce(X, W, t, reduction=reduction, grad_output=g)
+    _check(r, ref, "f32", reduction)
+    assert r.stats["n_valid"] == ref["n_valid"] == 230
+    assert r.stats["chunks_run"] == math.ceil(230 / chunk)
+    ign = (t == -100).numpy()
+    dx = r.dX.cpu().numpy()
+    assert np.all(dx[ign] == 0.0) and not np.signbit(dx[ign]).any()
+    if reduction == "none":
+        lo = r.loss.cpu().numpy()
+        assert np.all(lo[ign] == 0.0) and not np.signbit(lo[ign]).any()
+
+
+# ---------------------------------------------- 16-bit operands, ragged shapes
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("accum", ["same", "f32"])
+@pytest.mark.parametrize("shape", [(300, 256, 1000, 64), (77, 136, 1001, 32), (513, 384, 4099, 128)])
+def test_ragged_16bit(pkg, dtype, accum, shape):
+    BT, H, V, chunk = shape
+    seed = 2000 + BT
+    X, W, t = si.make_case(BT, H, V, dtype, seed, ignore="scattered", frac=0.1)
+    r = _run(pkg, X, W, t, reduction="mean", chunk_size=chunk,
+             accum_dtype=torch.float32 if accum == "f32" else None)
+    ref = oracle.flce(X, W, t, reduction="mean")
+    _check(r, ref, dtype, "mean")
+    assert r.dW.dtype == (torch.float32 if accum == "f32" else TD[dtype])
+
+
+@pytest.mark.parametrize("shape", [(300, 256, 1000, 64), (77, 136, 1001, 32)])
+def test_ragged_fp32(pkg, shape):
+    BT, H, V, chunk = shape
+    X, W, t = si.make_case(BT, H, V, "f32", 3000 + BT, ignore="scattered", frac=0.2)
+    g = si.make_grad_output(t, "sum", 3000 + BT, scalar=1.5)
+    r = _run(pkg, X, W, t, reduction="sum", chunk_size=chunk, grad_output=g)
+    ref = oracle.flce(X, W, t, reduction="sum", grad_output=g)
+    _check(r, ref, "f32", "sum")
+
+
+def test_split_grad_input_path(pkg):
+    """Few row tiles and a long vocabulary: grad_input runs split over V."""
+    BT, H, V = 64, 256, 8192
+    X, W, t = si.make_case(BT, H, V, "bf16", 4001, ignore="scattered", frac=0.1)
+    r = _run(pkg, X, W, t, reduction="mean", chunk_size=64, accum_dtype=torch.float32)
+    assert r.stats["dx_splits"] > 1
+    ref = oracle.flce(X, W, t, reduction="mean")
+    _check(r, ref, "bf16", "mean")
+
+
+# ------------------------------------------------------------- flags and modes
+def test_accumulate_into_given_grad_weight(pkg):
+    BT, H, V = 96, 128, 640
+    X, W, t = si.make_case(BT, H, V, "f32", 4002, ignore="scattered", frac=0.1)
+    init = torch.linspace(-1, 1, V * H, dtype=torch.float32).reshape(V, H)
+    r = _run(pkg, X, W, t, reduction="sum", chunk_size=32, dW_init=init)
+    ref = oracle.flce(X, W, t, reduction="sum", dW_init=init)
+    _check(r, ref, "f32", "sum")
+
+
+def test_frozen_weight(pkg):
+    BT, H, V = 200, 128, 900
+    X, W, t = si.make_case(BT, H, V, "bf16", 4003, ignore="prompt_first", frac=0.5, seq_len=100)
+    r = _run(pkg, X, W, t, reduction="sum", chunk_size=32, frozen_weight=True)
+    assert r.dW is None
+    ref = oracle.flce(X, W, t, reduction="sum", frozen=True)
+    _check(r, ref, "bf16", "sum", frozen=True)
+
+
+def test_none_with_per_token_upstream_and_nan_at_ignored(pkg):
+    BT, H, V = 160, 128, 700
+    X, W, t = si.make_case(BT, H, V, "bf16", 4004, ignore="prompt_first", frac=0.25, seq_len=40)
+    g = si.make_grad_output(t, "none", 4004, nan_at_ignored=True)
+    r = _run(pkg, X, W, t, reduction="none", chunk_size=32, grad_output=g)
+    ref = oracle.flce(X, W, t, reduction="none", grad_output=torch.nan_to_num(g))
+    _check(r, ref, "bf16", "none")
+    assert torch.isfinite(r.dW.float()).all() and torch.isfinite(r.dX.float()).all()
+
+
+def test_nan_in_ignored_rows_never_reaches_outputs(pkg):
+    """NaN-poisoned ignored X rows give bit-identical loss, dX and dW to the clean run."""
+    BT, H, V = 128, 128, 512
+    X, W, t = si.make_case(BT, H, V, "bf16", 4005, ignore="scattered", frac=0.3)
+    ign = t == -100
+    Xp = X.clone()
+    Xp[ign] = float("nan")
+    for red in ("mean", "none"):
+        a = _run(pkg, X, W, t, reduction=red, chunk_size=32, accum_dtype=torch.float32)
+        b = _run(pkg, Xp, W, t, reduction=red, chunk_size=32, accum_dtype=torch.float32)
+        assert torch.equal(a.loss.cpu(), b.loss.cpu())
+        assert torch.equal(a.dX.cpu(), b.dX.cpu())
+        assert torch.equal(a.dW.cpu(), b.dW.cpu())
+        assert (b.dX[ign.cuda()] == 0).all()
+
+
+def test_all_rows_ignored_and_empty_batch(pkg):
+    X, W, t = si.make_case(48, 64, 300, "bf16", 4006, ignore="all")
+    for red in ("mean", "sum"):
+        r = _run(pkg, X, W, t, reduction=red, chunk_size=16, accum_dtype=torch.float32)
+        assert float(r.loss) == 0.0 and r.stats["chunks_run"] == 0 and r.stats["n_valid"] == 0
+        assert (r.dX == 0).all() and (r.dW == 0).all()
+    X0, W0, t0 = si.make_case(0, 64, 300, "bf16", 4007)
+    r = _run(pkg, X0, W0, t0, reduction="mean", chunk_size=16)
+    assert float(r.loss) == 0.0 and (r.dW == 0).all()
+
+
+def test_ignored_rows_skip_whole_chunks_only(pkg):
+    """40 rows at chunk 16: 0/1/8/24/40 ignored rows give 3/3/2/1/0 chunks run."""
+    BT, H, V = 40, 64, 256
+    X, W, _ = si.make_case(BT, H, V, "f32", 4008)
+    base = si.make_targets(BT, V, 4008)
+    for n_ign, gemms in zip([0, 1, 8, 24, 40], [3, 3, 2, 1, 0]):
+        t = base.clone()
+        t[:n_ign] = -100
+        r = _run(pkg, X, W, t, reduction="sum", chunk_size=16, accum_dtype=torch.float32)
+        assert r.stats["chunks_run"] == gemms and r.stats["chunks_total"] == 3
+        assert r.stats["compacted"] == int(gemms < 3)
+        if n_ign < 40:
+            ref = oracle.flce(X, W, t, reduction="sum")
+            _check(r, ref, "f32", "sum")
+
+
+def test_ignore_index_inside_vocab(pkg):
+    BT, H, V = 64, 64, 128
+    X, W, t = si.make_case(BT, H, V, "f32", 4009)
+    t[::3] = 5
+    r = _run(pkg, X, W, t, reduction="mean", chunk_size=16, ignore_index=5)
+    ref = oracle.flce(X, W, t, reduction="mean", ignore_index=5)
+    assert r.stats["n_valid"] == ref["n_valid"]
+    _check(r, ref, "f32", "mean")
+
+
+def test_target_out_of_range_is_reported(pkg):
+    X, W, t = si.make_case(32, 64, 100, "bf16", 4010)
+    t[7] = 100
+    with pytest.raises(pkg.FlceError) as e:
+        _run(pkg, X, W, t, reduction="mean", chunk_size=16)
+    assert e.value.status == -3
+
+
+def test_loss_rows_identical_across_chunk_sizes(pkg):
+    """Per-row loss does not depend on the chunking (same k order for every row)."""
+    BT, H, V = 256, 256, 2000
+    X, W, t = si.make_case(BT, H, V, "bf16", 4011, ignore="scattered", frac=0.1)
+    outs = [_run(pkg, X, W, t, reduction="none", chunk_size=c, accum_dtype=torch.float32)
+            for c in (16, 64, 256)]
+    for o in outs[1:]:
+        assert torch.equal(o.loss.cpu(), outs[0].loss.cpu())
+        assert _rel(o.dX, outs[0].dX.double().cpu().numpy()) <= 1e-2
+        assert _rel(o.dW, outs[0].dW.double().cpu().numpy()) <= 1e-3
+
+
+def test_deterministic_run_to_run(pkg):
+    BT, H, V = 192, 256, 3000
+    X, W, t = si.make_case(BT, H, V, "bf16", 4012, ignore="scattered", frac=0.1)
+    a = _run(pkg, X, W, t, reduction="mean", chunk_size=64, accum_dtype=torch.float32)
+    b = _run(pkg, X, W, t, reduction="mean", chunk_size=64, accum_dtype=torch.float32)
+    assert torch.equal(a.loss.cpu(), b.loss.cpu())
+    assert torch.equal(a.dX.cpu(), b.dX.cpu()) and torch.equal(a.dW.cpu(), b.dW.cpu())
+
+
+def test_grad_weight_columns_sum_to_zero(pkg):
+    BT, H, V = 256, 128, 1024
+    X, W, t = si.make_case(BT, H, V, "f32", 4013, ignore="scattered", frac=0.1)
+    r = _run(pkg, X, W, t, reduction="sum", chunk_size=64)
+    col = r.dW.double().sum(0).abs().max().item()
+    assert col <= 1e-4 * r.dW.double().abs().sum(0).max().item()
+
+
+def test_autograd_wrapper_matches_oracle(pkg):
+    BT, H, V = 128, 128, 800
+    X, W, t = si.make_case(BT, H, V, "bf16", 4014, ignore="scattered", frac=0.1)
+    dev = torch.device("cuda:0")
+    x = X.to(dev).requires_grad_(True)
+    w = W.to(dev).requires_grad_(True)
+    for red in ("mean", "none"):
+        x.grad = None
+        w.grad = None
+        loss = pkg.fused_linear_cross_entropy(x, w, t.to(dev), reduction=red, chunk_size=32,
+                                              accum_dtype=torch.float32)
+        if red == "mean":
+            (loss * 2.0).backward()
+            ref = oracle.flce(X, W, t, reduction="mean", grad_output=torch.tensor([2.0]))
+        else:
+            g = si.make_grad_output(t, "none", 4014, nan_at_ignored=False)
+            loss.backward(g.to(dev))
+            ref = oracle.flce(X, W, t, reduction="none", grad_output=g)
+        torch.cuda.synchronize()
+        assert w.grad.dtype == torch.bfloat16
+        assert _rel(x.grad, ref["dX"]) <= 2e-2
+        assert _rel(w.grad, ref["dW"]) <= 2e-2
