@@ -1,0 +1,249 @@
+"""Benchmark: fused linear cross-entropy forward + backward on one MI355X.
+
+One step = one flce_fwd_bwd call over one batch (row compaction, the chunk
+loop of logits GEMM -> softmax-gradient -> grad_input GEMM -> grad_weight
+GEMM, loss reduction).  Default workload: the Llama-3-8B lm_head shape,
+bf16, BT 8192, H 4096, V 128256, all rows labelled, mean, fp32 grad_weight,
+chunk_size 2048; the 256-row chunk geometry is measured too and reported
+under "extra".  Inputs are seeded synthetic tensors already resident in HBM
+when the timed region starts.
+
+Prints one JSON line.  ``value`` = tokens/s of the whole job (BT x steps /
+elapsed).  ``roofline`` is for the dominant kernel, with its average launch
+duration measured by HIP events on the stream it runs on, over the timed
+steps.  ``cpu_baseline`` times the fp64 oracle on a bounded sample of rows of
+the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # MI355X dense
+HBM_PEAK_GBS = 8000.0
+METRIC = "FLCE fwd+bwd tokens/sec + % bf16 MFMA peak @BT=8192,H=4096,V=128256"
+
+WORKLOADS = {
+    # name: BT, H, V, dtype, accum, reduction, chunk, labelled share
+    "llama3_8b_lm_head": dict(BT=8192, H=4096, V=128256, dtype="bf16", accum="f32",
+                              reduction="mean", chunk=2048, share=1.0, seed=1001),
+    "llama3_8b_lm_head_c256": dict(BT=8192, H=4096, V=128256, dtype="bf16", accum="f32",
+                                   reduction="mean", chunk=256, share=1.0, seed=1001),
+    "same_dtype_sweep_bf16": dict(BT=16384, H=4096, V=32000, dtype="bf16", accum="same",
+                                  reduction="mean", chunk=0, share=1.0, seed=1002),
+    "same_dtype_sweep_f16": dict(BT=16384, H=4096, V=32000, dtype="f16", accum="same",
+                                 reduction="mean", chunk=0, share=1.0, seed=1002),
+    "same_dtype_sweep_f32": dict(BT=16384, H=4096, V=32000, dtype="f32", accum="same",
+                                 reduction="mean", chunk=0, share=1.0, seed=1002),
+    "long_seq_8k_c256": dict(BT=8192, H=5376, V=262144, dtype="bf16", accum="same",
+                             reduction="mean", chunk=256, share=1.0, seed=1003),
+    "long_seq_8k_default": dict(BT=8192, H=5376, V=262144, dtype="bf16", accum="same",
+                                reduction="mean", chunk=0, share=1.0, seed=1003),
+    "long_seq_32k_c256": dict(BT=32768, H=5376, V=262144, dtype="bf16", accum="same",
+                              reduction="mean", chunk=256, share=1.0, seed=1003),
+    "long_seq_32k_default": dict(BT=32768, H=5376, V=262144, dtype="bf16", accum="same",
+                                 reduction="mean", chunk=0, share=1.0, seed=1003),
+    **{f"masked_sft_{int(s * 100)}_{mode}": dict(BT=8192, H=2048, V=151936, dtype="bf16",
+                                                 accum="same", reduction="sum", chunk=0, share=s,
+                                                 seed=1004, frozen=(mode == "frozen"))
+       for s in (1.0, 0.75, 0.5, 0.1) for mode in ("trained", "frozen")},
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="llama3_8b_lm_head", choices=sorted(WORKLOADS))
+    p.add_argument("--extra", default="llama3_8b_lm_head_c256",
+                   help="comma-separated extra workloads reported under 'extra' ('' for none)")
+    p.add_argument("--cpu-rows", type=int, default=16, help="rows in the oracle's timed sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_inputs(cfg, dev):
+    import torch
+    import synthetic_inputs as si
+    BT, H, V = cfg["BT"], cfg["H"], cfg["V"]
+    log(f"generating inputs BT={BT} H={H} V={V} {cfg['dtype']}")
+    t0 = time.perf_counter()
+    X = si.make_x(BT, H, cfg["dtype"], cfg["seed"])
+    W = si.make_w(V, H, cfg["dtype"], cfg["seed"])
+    share = cfg["share"]
+    if share >= 1.0:
+        t = si.make_targets(BT, V, cfg["seed"])
+    else:
+        t = si.make_targets(BT, V, cfg["seed"], ignore="prompt_first", frac=1.0 - share,
+                            seq_len=BT)
+    host = (X, W, t)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    return host, (X.to(dev), W.to(dev), t.to(dev))
+
+
+def run_workload(name, cfg, steps, warmup, dev, host_dev=None):
+    import torch
+    import linear_cross_entropy_chunked_amd as pkg
+    BT, H, V = cfg["BT"], cfg["H"], cfg["V"]
+    host, (X, W, t) = host_dev if host_dev is not None else make_inputs(cfg, dev)
+    dt = {"bf16": pkg.BF16, "f16": pkg.F16, "f32": pkg.F32}[cfg["dtype"]]
+    adt = pkg.F32 if cfg["accum"] == "f32" else dt
+    frozen = bool(cfg.get("frozen", False))
+    red = pkg.REDUCTIONS[cfg["reduction"]]
+    tdt = {pkg.F32: torch.float32, pkg.F16: torch.float16, pkg.BF16: torch.bfloat16}
+    loss = torch.empty(BT if red == pkg.NONE else 1, dtype=torch.float32, device=dev)
+    dX = torch.empty_like(X)
+    dW = None if frozen else torch.empty(V, H, dtype=tdt[adt], device=dev)
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    wsb = pkg.flce_workspace_bytes(BT, H, V, dt, cfg["chunk"], 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    st = pkg.FlceStats()
+
+    def step():
+        rc = pkg.flce_fwd_bwd(X.data_ptr(), W.data_ptr(), t.data_ptr(), BT, H, V, dt, -100, red,
+                              cfg["chunk"], 1, adt, int(frozen), 0, None, loss.data_ptr(),
+                              dX.data_ptr(), None if frozen else dW.data_ptr(), ws.data_ptr(),
+                              wsb, stream.cuda_stream, st)
+        if rc != 0:
+            raise pkg.FlceError(rc, "flce_fwd_bwd")
+
+    log(f"{name}: {warmup} warmup step(s)")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"{name}: {steps} timed step(s)")
+    pkg.flce_profile_begin()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = pkg.flce_profile_end()
+    peak_transient = torch.cuda.max_memory_allocated(dev) - mem0
+    del ws
+    n_lab = st.n_valid
+    flops = (4 if frozen else 6) * n_lab * H * V
+    ms = elapsed / steps * 1e3
+    res = dict(
+        workload=name, BT=BT, H=H, V=V, dtype=cfg["dtype"], accum_dtype=cfg["accum"],
+        reduction=cfg["reduction"], frozen_weight=frozen, labelled_share=cfg["share"],
+        chunk_size=st.chunk_size, chunks_run=st.chunks_run, dx_splits=st.dx_splits,
+        n_valid=n_lab, ms_per_step=ms, tokens_per_s=BT * steps / elapsed,
+        algorithmic_tflops=flops / (ms * 1e-3) / 1e12,
+        mfma_frac=flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[cfg["dtype"]],
+        workspace_bytes=wsb, peak_transient_bytes=int(peak_transient),
+        kernels={k: dict(launches=v[0] // steps, ms_per_launch=(v[1] / v[0] if v[0] else 0.0),
+                         ms_per_step=v[1] / steps)
+                 for k, v in prof.items() if v[0]},
+    )
+    return res, host
+
+
+def roofline(res, cfg):
+    """Roofline figures of the dominant kernel of one step."""
+    c, H, V = res["chunk_size"], res["H"], res["V"]
+    name, k = max(res["kernels"].items(), key=lambda kv: kv[1]["ms_per_step"])
+    s = 4 if cfg["dtype"] == "f32" else 2
+    if name in ("logits_gemm", "dx_gemm", "dw_gemm"):
+        # per launch: one full chunk of c rows -> 2 c H V flops
+        rows = min(c, res["n_valid"])
+        work = 2.0 * rows * H * V
+        achieved = work / (k["ms_per_launch"] * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[cfg["dtype"]]
+        return dict(kernel=name, bound="mfma", achieved=achieved, peak=peak, unit="TFLOP/s",
+                    frac=achieved / peak, traffic=None,
+                    work_per_launch=f"2*c*H*V flops = {work:.4g} (c={rows})")
+    # bandwidth-bound kernels: softmax reads + writes the slab once
+    rows = min(c, res["n_valid"])
+    byts = 2.0 * rows * V * s
+    achieved = byts / (k["ms_per_launch"] * 1e-3) / 1e9
+    return dict(kernel=name, bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=achieved / HBM_PEAK_GBS, traffic=None,
+                work_per_launch=f"2*c*V*itemsize bytes = {byts:.4g}")
+
+
+def cpu_baseline(host, cfg, rows):
+    """fp64 loop oracle on the first `rows` rows of the same batch (full H and V)."""
+    import numpy as np
+    import oracle
+    X, W, t = host
+    Xs, ts = X[:rows], t[:rows]
+    log(f"cpu baseline: widening inputs, then {rows} rows through the oracle")
+    Xd, Wd = oracle.widen(Xs), oracle.widen(W)
+    t0 = time.perf_counter()
+    oracle.flce(Xd, Wd, ts, reduction=cfg["reduction"], frozen=bool(cfg.get("frozen", False)))
+    dt = time.perf_counter() - t0
+    return dict(value=rows / dt, unit="tokens/s", cores=oracle.threads(), kind="oracle",
+                sample=f"first {rows} of {cfg['BT']} rows of the same batch through the fp64 "
+                       f"loop oracle (forward + backward, full H={cfg['H']}, V={cfg['V']}); "
+                       f"{dt:.1f} s; widening the inputs to fp64 is not timed")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {a.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import linear_cross_entropy_chunked_amd as pkg
+    pkg.load()
+    dev = torch.device("cuda:0")
+    cfg = WORKLOADS[a.workload]
+    main_res, host = run_workload(a.workload, cfg, a.steps, a.warmup, dev)
+    extras = {}
+    for name in [e for e in a.extra.split(",") if e and e != a.workload]:
+        ecfg = WORKLOADS[name]
+        same = all(ecfg[k] == cfg[k] for k in ("BT", "H", "V", "dtype", "seed", "share"))
+        hd = None
+        if same:
+            X, W, t = host
+            hd = (host, (X.to(dev), W.to(dev), t.to(dev)))
+        extras[name], _ = run_workload(name, ecfg, max(a.steps // 2, 2), a.warmup, dev, hd)
+    rl = roofline(main_res, cfg)
+    out = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": a.workload, "BT": cfg["BT"], "H": cfg["H"], "V": cfg["V"],
+                   "chunk_size": main_res["chunk_size"], "accum_dtype": cfg["accum"],
+                   "reduction": cfg["reduction"], "labelled_share": cfg["share"],
+                   "frozen_weight": main_res["frozen_weight"]},
+        "mfma_frac_of_peak": main_res["mfma_frac"],
+        "algorithmic_tflops": main_res["algorithmic_tflops"],
+        "roofline": rl,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(host, cfg, a.cpu_rows)
+    out["detail"] = main_res
+    out["extra"] = extras
+    out["context"] = ("pages' figures on other hardware (not targets): BT 8192, H 4096, "
+                      "V 128256 bf16 on H200, chunk 256: 53.039 ms; chunk 2048: 37.748 ms")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

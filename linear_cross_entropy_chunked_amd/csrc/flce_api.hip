@@ -48,7 +48,8 @@ int64_t chunk_rows(int64_t BT, int64_t H, int64_t V, int64_t chunk_size, int32_t
 
 // ---------------------------------------------------------- workspace layout
 constexpr int64_t kAlign = 256;
-constexpr int kDxTargetBlocks = 512;     // aim for two workgroups per CU on 256 CUs
+constexpr uint64_t kMaxOperandBytes = 0x7fff0000ull;  // 2 GiB - 64 KiB
+constexpr int kDxTargetBlocks = 256;     // one workgroup per CU on 256 CUs
 constexpr int64_t kDxMinKPerSplit = 1024;
 constexpr int kDxMaxSplits = 32;
 
@@ -66,8 +67,8 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t c) {
   Layout L;
   L.c = c;
   L.ldz = round_up(V, 8);
-  L.stats_ld = ceil_div(V, stats_cols_per_block());
-  const int64_t tiles = ceil_div(c, gemm_block_m()) * ceil_div(H, gemm_block_n());
+  L.stats_ld = ceil_div(V, stats_cols());
+  const int64_t tiles = ceil_div(c, dx_tile_m((int)c, H)) * ceil_div(H, dx_tile_n((int)c, H));
   int64_t splits = ceil_div(kDxTargetBlocks, tiles);
   const int64_t by_k = L.ldz / kDxMinKPerSplit;
   if (splits > by_k) splits = by_k;
@@ -262,6 +263,8 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
   if (!frozen_weight && (!dW || !aligned(dW, 16))) return FLCE_E_ARG;
   if (BT > 0 && (!X || !W || !targets || !dX)) return FLCE_E_ARG;
   if (BT > 0 && (!aligned(X, 16) || !aligned(W, 16) || !aligned(dX, 16))) return FLCE_E_ARG;
+  // The kernels address X and the logits slab with 32-bit byte offsets.
+  if ((uint64_t)BT * (uint64_t)H * itemsize(dtype) > kMaxOperandBytes) return FLCE_E_ARG;
   const int64_t c = chunk_rows(BT, H, V, chunk_size, chunk_mem_const);
   if (c < 1) return FLCE_E_ARG;
   const Layout L = make_layout(BT, H, V, dtype, c);
@@ -323,7 +326,6 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
     FLCE_LAUNCH(FLCE_K_FILL, launch_fill_zero(dW, V * H * (int64_t)itemsize(dw_dt), st));
 
   const float inv_n = N > 0 ? 1.0f / (float)N : 0.f;
-  const int64_t stats_n = L.stats_ld;
 
   // softmax pass geometry: enough workgroups to cover the chip, >= 2048 columns each
   int parts = (int)ceil_div(2048, c);
@@ -344,6 +346,7 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
     la.idx = cidx;
     la.targets = targets;
     la.rows = rows;
+    la.BT = BT;
     la.H = H;
     la.V = V;
     la.slab = slab;
@@ -360,7 +363,7 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
     sa.rows = rows;
     sa.stats = stats_buf;
     sa.stats_ld = L.stats_ld;
-    sa.stats_n = stats_n;
+    sa.stats_n = L.stats_ld;
     sa.ztgt = ztgt;
     sa.idx = cidx;
     sa.targets = targets;
@@ -410,6 +413,7 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
       wa.X = X;
       wa.idx = cidx;
       wa.rows = rows;
+      wa.BT = BT;
       wa.H = H;
       wa.V = V;
       wa.ldz = L.ldz;

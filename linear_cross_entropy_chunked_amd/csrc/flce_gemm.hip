@@ -2,141 +2,181 @@
 // for gfx950 (v0.8.3 commit bad6c3ec42, Summary: reusable logits, direct dX,
 // direct dW; PR #1554, Summary: logits, grad_input and grad_weight GEMMs):
 //
-//   logits  Z[m, n]  = sum_k X[idx[m], k] * W[n, k]        (A K-contiguous, B K-contiguous)
-//   dX      dX[idx[m], n] = s * sum_k G[m, k] * W[k, n]    (A K-contiguous, B N-contiguous)
-//   dW      dW[m, n] (+)= s * sum_k G[k, m] * X[idx[k], n] (A M-contiguous, B N-contiguous)
+//   logits  Z[m, n]  = sum_k X[idx[m], k] * W[n, k]        (A k-contiguous, B k-contiguous)
+//   dX      dX[idx[m], n] = s * sum_k G[m, k] * W[k, n]    (A k-contiguous, B n-contiguous)
+//   dW      dW[m, n] (+)= s * sum_k G[k, m] * X[idx[k], n] (A m-contiguous, B n-contiguous)
 //
-// All three share one main loop: 128x128 block tiles, four waves of 64x64,
-// 32x32 MFMA tiles, both operands staged through LDS in a k-contiguous layout
-// so that each lane reads its MFMA fragment with one 16-byte LDS read.
-// Operands that are contiguous along M or N in memory are transposed in
-// registers (4 k-rows x one 16-byte vector) on their way into LDS.  Two LDS
+// One main loop serves all three.  Both operands are staged through LDS in a
+// k-contiguous layout (rows padded by 16 bytes), so each lane reads an MFMA
+// fragment with one 16-byte LDS read and 8 consecutive lanes hit 8 distinct
+// bank groups.  Operands that are contiguous along M or N in memory are
+// transposed in registers in 8x8 (16-bit) or 4x4 (fp32) blocks; lanes are
+// laid out k-block fastest so that both the global loads (128 contiguous
+// bytes per row) and the 16-byte LDS writes are conflict-free.  Two LDS
 // buffers: the next k-tile's global loads are in flight while the current
-// tile is multiplied.
+// one is multiplied.
+//
+// Two tile shapes: 256x256 blocks of four 128x128 waves (one workgroup per
+// CU, 144 KiB of LDS) for the compute-bound shapes, and 128x128 blocks of four
+// 64x64 waves (two workgroups per CU) where the problem is small or, for
+// grad_weight with few rows per chunk, bound by the read-modify-write of dW.
+#include <type_traits>
+
 #include "flce_device.hpp"
 #include "flce_internal.h"
 
 namespace flce {
 
-constexpr int BM = 128, BN = 128;
-constexpr int WAVES_M = 2, WAVES_N = 2;
-constexpr int NT = 64 * WAVES_M * WAVES_N;
-constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // 64 x 64 per wave
-constexpr int FM = WTM / 32, FN = WTN / 32;            // 2 x 2 MFMA tiles per wave
+template <int BM_, int BN_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int WAVES_M = 2, WAVES_N = 2;
+  static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+};
+typedef Cfg<256, 256> Big;
+typedef Cfg<128, 128> Small;
 
 template <class T>
-struct Tile {
+struct KT {  // k-tile geometry per element type
   typedef typename T::storage S;
   static constexpr int BK = (sizeof(S) == 2) ? 64 : 32;
-  static constexpr int LDK = BK + ((sizeof(S) == 2) ? 8 : 4);  // padded LDS row (elements)
-  static constexpr int A_ELEMS = BM * LDK;
-  static constexpr int B_ELEMS = BN * LDK;
-  static constexpr size_t LDS_BYTES = 2 * (A_ELEMS + B_ELEMS) * sizeof(S);
+  static constexpr int LDK = BK + 16 / (int)sizeof(S);  // padded LDS row (elements)
+};
+
+template <class T, class C>
+struct Lds {
+  static constexpr int A_ELEMS = C::BM * KT<T>::LDK;
+  static constexpr int B_ELEMS = C::BN * KT<T>::LDK;
+  static constexpr size_t OPERANDS = 2 * (size_t)(A_ELEMS + B_ELEMS) * sizeof(typename T::storage);
+  // the epilogue stages WTM x (BN + 4) fp32 in the same memory
+  static constexpr size_t STAGE = (size_t)C::WTM * (C::BN + 4) * sizeof(float);
+  static constexpr size_t BYTES = OPERANDS > STAGE ? OPERANDS : STAGE;
 };
 
 // ---------------------------------------------------------------------------
-// Operand tile loaders.  Each fills an R x BK tile of LDS laid out [R][LDK]
-// (k contiguous).
+// Operand tile loaders.  Each fills an R x BK tile of LDS laid out [R][LDK].
+// Global reads are raw buffer loads: a wave-uniform descriptor (base, byte
+// range) plus a 32-bit per-lane byte offset; any offset at or past the range
+// reads as zero, which is how rows and columns outside the problem are
+// masked (an out-of-range lane gets kOOB).
 // ---------------------------------------------------------------------------
+constexpr uint32_t kOOB = 0xfffffff0u;
 
-// Source already k-contiguous: row r of the tile starts at rowp(r) (nullptr:
-// a zero row).  Vectors whose first k is >= kend read as zero; callers keep
-// kend a multiple of the vector width, and any element between the logical
-// K and kend is zero in memory.
-template <class T, int R>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0x7ffffff0ull ? 0x7ffffff0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// Source already k-contiguous: tile row r starts at byte offset rowoff(r)
+// (kOOB: zero row) of the descriptor.  Vectors whose first k is >= kend read
+// as zero; callers keep kend a multiple of the vector width, and elements
+// between the logical K and kend are zero in memory.
+template <class T, int R, int NT>
 struct KRowsLoader {
   typedef typename T::storage S;
-  static constexpr int BK = Tile<T>::BK;
+  static constexpr int BK = KT<T>::BK;
   static constexpr int VPR = BK / T::vec;
   static constexpr int NV = R * VPR / NT;
   static_assert((R * VPR) % NT == 0, "tile not divisible among threads");
   u32x4_t reg[NV];
-  const S* ptr[NV];
+  uint32_t roff[NV];
   int kofs[NV];
   int lrow[NV];
 
   template <class RowFn>
-  __device__ void init(int tid, RowFn rowp) {
+  __device__ void init(int tid, RowFn rowoff) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = tid + i * NT;
       lrow[i] = v / VPR;
       kofs[i] = (v % VPR) * T::vec;
-      ptr[i] = rowp(lrow[i]);
+      roff[i] = rowoff(lrow[i]);
     }
   }
-  __device__ void load(int k0, int kend) {
+  __device__ void load(__amdgpu_buffer_rsrc_t rs, int k0, int kend) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int k = k0 + kofs[i];
-      if (ptr[i] != nullptr && k < kend)
-        reg[i] = *reinterpret_cast<const u32x4_t*>(ptr[i] + k);
-      else
-        reg[i] = u32x4_t{0u, 0u, 0u, 0u};
+      const uint32_t off =
+          (roff[i] != kOOB && k < kend) ? roff[i] + (uint32_t)k * (uint32_t)sizeof(S) : kOOB;
+      reg[i] = buf_load16(rs, off);
     }
   }
   __device__ void store(S* lds) const {
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      *reinterpret_cast<u32x4_t*>(lds + lrow[i] * Tile<T>::LDK + kofs[i]) = reg[i];
+      *reinterpret_cast<u32x4_t*>(lds + lrow[i] * KT<T>::LDK + kofs[i]) = reg[i];
   }
 };
 
-// Source contiguous along the tile's row index: element (r, k) of the tile is
-// kptr(k)[c0 + r], with kptr(k) == nullptr for a zero k-row and columns at or
-// past cend reading as zero (vector granularity, as above).  Each thread moves
-// 4 k-rows x one 16-byte vector and transposes them in registers.
-template <class T, int R>
+// Source contiguous along the tile's row index: tile element (r, k) sits at
+// byte offset rowoff(k) + (c0 + r) * sizeof(S) of the descriptor, rowoff(k) ==
+// kOOB for a zero k-row; columns at or past cend read as zero (vector
+// granularity).  Each thread moves a TK x TK block (TK = elements per 16
+// bytes: 8 k-rows x 8 columns for 16-bit types, 4 x 4 for fp32) and
+// transposes it in registers.  Lane order is k-block fastest, so a wave's
+// global reads cover 128 contiguous bytes per row and its 16-byte LDS writes
+// fall in distinct banks.
+template <class T, int R, int NT>
 struct KColsLoader {
   typedef typename T::storage S;
-  static constexpr int BK = Tile<T>::BK;
-  static constexpr int CB = R / T::vec;   // column blocks
-  static constexpr int KB = BK / 4;       // k blocks of 4 rows
-  static constexpr int NB = CB * KB / NT; // blocks per thread
-  static_assert((CB * KB) % NT == 0, "tile not divisible among threads");
-  u32x4_t reg[NB][4];
+  static constexpr int TK = T::vec;
+  static constexpr int BK = KT<T>::BK;
+  static constexpr int KBN = BK / TK;             // k blocks per tile
+  static constexpr int NBLK = (R / TK) * KBN;     // blocks per tile
+  static constexpr int NB = (NBLK + NT - 1) / NT; // blocks per thread
+  u32x4_t reg[NB][TK];
   int cb[NB], kb[NB];
+  bool act[NB];
 
   __device__ void init(int tid) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int b = tid + i * NT;
-      cb[i] = b % CB;
-      kb[i] = b / CB;
+      act[i] = b < NBLK;
+      kb[i] = b % KBN;
+      cb[i] = b / KBN;
     }
   }
   template <class KFn>
-  __device__ void load(int k0, KFn kptr, int c0, int cend) {
+  __device__ void load(__amdgpu_buffer_rsrc_t rs, int k0, KFn rowoff, int c0, int cend) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int c = c0 + cb[i] * T::vec;
+      const int c = c0 + cb[i] * TK;
+      const bool col_ok = act[i] && c < cend;
+      const uint32_t cofs = (uint32_t)c * (uint32_t)sizeof(S);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const S* p = kptr(k0 + kb[i] * 4 + q);
-        if (p != nullptr && c < cend)
-          reg[i][q] = *reinterpret_cast<const u32x4_t*>(p + c);
-        else
-          reg[i][q] = u32x4_t{0u, 0u, 0u, 0u};
+      for (int q = 0; q < TK; ++q) {
+        const uint32_t ro = rowoff(k0 + kb[i] * TK + q);
+        reg[i][q] = buf_load16(rs, (col_ok && ro != kOOB) ? ro + cofs : kOOB);
       }
     }
   }
   __device__ void store(S* lds) const {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      S* base = lds + (cb[i] * T::vec) * Tile<T>::LDK + kb[i] * 4;
+      if (!act[i]) continue;
+      S* base = lds + (cb[i] * TK) * KT<T>::LDK + kb[i] * TK;
       if constexpr (sizeof(S) == 2) {
-        // reg[i][q] holds 8 columns of k-row q as 4 dwords (2 columns each).
+        // reg[i][q] = k-row q, columns 0..7 (dword d: columns 2d | 2d+1 << 16).
+        // Column n, as 8 k values: dword e = k 2e | k 2e+1 << 16.
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const uint32_t r0 = reg[i][0][d], r1 = reg[i][1][d], r2 = reg[i][2][d], r3 = reg[i][3][d];
-          // column 2d: low halves; column 2d+1: high halves
-          u32x2_t lo, hi;
-          lo[0] = (r0 & 0xffffu) | (r1 << 16);
-          lo[1] = (r2 & 0xffffu) | (r3 << 16);
-          hi[0] = (r0 >> 16) | (r1 & 0xffff0000u);
-          hi[1] = (r2 >> 16) | (r3 & 0xffff0000u);
-          *reinterpret_cast<u32x2_t*>(base + (2 * d) * Tile<T>::LDK) = lo;
-          *reinterpret_cast<u32x2_t*>(base + (2 * d + 1) * Tile<T>::LDK) = hi;
+          u32x4_t lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t x = reg[i][2 * e][d], y = reg[i][2 * e + 1][d];
+            lo[e] = (x & 0xffffu) | (y << 16);
+            hi[e] = (x >> 16) | (y & 0xffff0000u);
+          }
+          *reinterpret_cast<u32x4_t*>(base + (2 * d) * KT<T>::LDK) = lo;
+          *reinterpret_cast<u32x4_t*>(base + (2 * d + 1) * KT<T>::LDK) = hi;
         }
       } else {
 #pragma unroll
@@ -146,7 +186,7 @@ struct KColsLoader {
           col[1] = reg[i][1][d];
           col[2] = reg[i][2][d];
           col[3] = reg[i][3][d];
-          *reinterpret_cast<u32x4_t*>(base + d * Tile<T>::LDK) = col;
+          *reinterpret_cast<u32x4_t*>(base + d * KT<T>::LDK) = col;
         }
       }
     }
@@ -154,60 +194,168 @@ struct KColsLoader {
 };
 
 // ---------------------------------------------------------------------------
-// One BK-deep step of the wave's 64x64 tile from LDS.
+// One BK-deep step of the wave's tile from LDS.
 // ---------------------------------------------------------------------------
-template <class T>
+template <class T, class C>
 __device__ __forceinline__ void mma_tile(const typename T::storage* As,
                                          const typename T::storage* Bs, int wm, int wn,
-                                         int lane, f32x16_t (&acc)[FM][FN]) {
-  constexpr int BK = Tile<T>::BK, LDK = Tile<T>::LDK;
+                                         int lane, f32x16_t (&acc)[C::FM][C::FN]) {
+  constexpr int BK = KT<T>::BK, LDK = KT<T>::LDK;
   const int r32 = lane & 31, hk = lane >> 5;
 #pragma unroll
   for (int s = 0; s < BK / T::kstep; ++s) {
     if constexpr (sizeof(typename T::storage) == 2) {
-      u32x4_t fa[FM], fb[FN];
+      u32x4_t fa[C::FM], fb[C::FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        fa[i] = *reinterpret_cast<const u32x4_t*>(As + (wm * WTM + i * 32 + r32) * LDK +
+      for (int i = 0; i < C::FM; ++i)
+        fa[i] = *reinterpret_cast<const u32x4_t*>(As + (wm * C::WTM + i * 32 + r32) * LDK +
                                                    s * 16 + hk * 8);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        fb[j] = *reinterpret_cast<const u32x4_t*>(Bs + (wn * WTN + j * 32 + r32) * LDK +
+      for (int j = 0; j < C::FN; ++j)
+        fb[j] = *reinterpret_cast<const u32x4_t*>(Bs + (wn * C::WTN + j * 32 + r32) * LDK +
                                                    s * 16 + hk * 8);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) T::mma(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < C::FN; ++j) T::mma(fa[i], fb[j], acc[i][j]);
     } else {
-      float fa[FM], fb[FN];
+      float fa[C::FM], fb[C::FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = As[(wm * WTM + i * 32 + r32) * LDK + s * 2 + hk];
+      for (int i = 0; i < C::FM; ++i)
+        fa[i] = As[(wm * C::WTM + i * 32 + r32) * LDK + s * 2 + hk];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = Bs[(wn * WTN + j * 32 + r32) * LDK + s * 2 + hk];
+      for (int j = 0; j < C::FN; ++j)
+        fb[j] = Bs[(wn * C::WTN + j * 32 + r32) * LDK + s * 2 + hk];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) T::mma(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < C::FN; ++j) T::mma(fa[i], fb[j], acc[i][j]);
     }
   }
 }
 
-// Row / column of accumulator element r of MFMA tile (i, j) in the block tile
-// (32x32 MFMA output layout: column = lane % 32; row = 8*(r/4) + 4*(lane/32) + r%4).
-__device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
-  return wm * WTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-}
-__device__ __forceinline__ int acc_col(int wn, int j, int lane) {
-  return wn * WTN + j * 32 + (lane & 31);
+// The double-buffered k loop shared by the three kernels.
+template <class T, class C, class LA, class LB, class LoadA, class LoadB>
+__device__ __forceinline__ void main_loop(LA& la, LB& lb, LoadA load_a, LoadB load_b, int nk,
+                                          typename T::storage* As, typename T::storage* Bs,
+                                          int wm, int wn, int lane,
+                                          f32x16_t (&acc)[C::FM][C::FN]) {
+  constexpr int BK = KT<T>::BK;
+  if (nk <= 0) return;
+  load_a(0);
+  load_b(0);
+  la.store(As);
+  lb.store(Bs);
+  __syncthreads();
+  for (int t = 0; t < nk; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < nk) {
+      load_a((t + 1) * BK);
+      load_b((t + 1) * BK);
+    }
+    mma_tile<T, C>(As + cur * Lds<T, C>::A_ELEMS, Bs + cur * Lds<T, C>::B_ELEMS, wm, wn, lane,
+                   acc);
+    if (t + 1 < nk) {
+      la.store(As + (cur ^ 1) * Lds<T, C>::A_ELEMS);
+      lb.store(Bs + (cur ^ 1) * Lds<T, C>::B_ELEMS);
+    }
+    __syncthreads();
+  }
 }
 
-__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[FM][FN]) {
+template <class C>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::FM][C::FN]) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < C::FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+// Epilogue through LDS.  After the main loop the operand buffers are free;
+// the accumulators of one row of waves (WTM x BN fp32) are written there in
+// fully unrolled code (32x32 MFMA output layout: element r of a lane sits at
+// column lane % 32, row 8*(r/4) + 4*(lane/32) + r%4 of its 32x32 tile), then every thread walks 8-column pieces of those rows:
+// fn(block_row, block_col, v[8]).  Consecutive lanes take consecutive pieces
+// of a row, so 8 aligned lanes cover one 64-column block and global accesses
+// are 16-byte vectors.  Every lane of every wave runs the same number of
+// pieces, so fn may use cross-lane operations within groups of 8 lanes.
+template <class C>
+struct Stage {
+  static constexpr int LS = C::BN + 4;  // staged row stride in floats (16-byte pad)
+  static constexpr int SUBS = C::BN / 8;
+  static constexpr size_t BYTES = (size_t)C::WTM * LS * sizeof(float);
+  static_assert((C::WTM * SUBS) % C::NT == 0, "uniform piece count per lane");
+};
+
+template <class C, class Fn>
+__device__ __forceinline__ void staged_epilogue(float* stage, const f32x16_t (&acc)[C::FM][C::FN],
+                                                int wm, int wn, int lane, int tid, Fn fn) {
+  constexpr int LS = Stage<C>::LS, SUBS = Stage<C>::SUBS;
+  for (int p = 0; p < C::WAVES_M; ++p) {
+    __syncthreads();
+    if (wm == p) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int col = wn * C::WTN + j * 32 + (lane & 31);
+            stage[row * LS + col] = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+    for (int q = tid; q < C::WTM * SUBS; q += C::NT) {
+      const int lrow = q / SUBS, piece = q % SUBS;
+      const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8);
+      const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8 + 4);
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      fn(p * C::WTM + lrow, piece * 8, v);
+    }
+  }
+}
+
+// Pack 8 floats into one 16-byte vector of the storage type.
+template <class T>
+__device__ __forceinline__ u32x4_t pack8(const float (&v)[8]) {
+  u32x4_t o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = (uint32_t)T::from_f32(v[2 * e]) | ((uint32_t)T::from_f32(v[2 * e + 1]) << 16);
+  return o;
+}
+template <class T>
+__device__ __forceinline__ void unpack8(const u32x4_t& x, float (&v)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = T::to_f32((u16)(x[e] & 0xffffu));
+    v[2 * e + 1] = T::to_f32((u16)(x[e] >> 16));
+  }
+}
+
+// Store 8 consecutive values (16-bit: one 16-byte store; fp32: two).
+template <class T>
+__device__ __forceinline__ void store8(typename T::storage* p, const float (&v)[8]) {
+  if constexpr (sizeof(typename T::storage) == 2) {
+    *reinterpret_cast<u32x4_t*>(p) = pack8<T>(v);
+  } else {
+    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4_t*>(p + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+  }
+}
+
+__device__ __forceinline__ float group8_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1, kWave));
+  v = fmaxf(v, __shfl_xor(v, 2, kWave));
+  return fmaxf(v, __shfl_xor(v, 4, kWave));
+}
+__device__ __forceinline__ float group8_sum(float v) {
+  v += __shfl_xor(v, 1, kWave);
+  v += __shfl_xor(v, 2, kWave);
+  return v + __shfl_xor(v, 4, kWave);
 }
 
 // Upstream scale s for mean / sum (grad_output may be NULL = 1).
@@ -219,136 +367,104 @@ __device__ __forceinline__ float upstream_scale(const float* grad_output, float 
 }
 
 // ---------------------------------------------------------------------------
-// Logits: slab[m, n] = X[idx[m], :] . W[n, :], plus per-(row, 64-column block)
-// running max and sum of exp, and the target logit in fp32.
+// Logits: slab[m, n] = X[idx[m], :] . W[n, :], plus per-(row, wave column
+// block) running max and sum of exp, and the target logit in fp32.
 // ---------------------------------------------------------------------------
-template <class T>
-__global__ __launch_bounds__(NT) void logits_kernel(LogitsArgs a) {
+template <class T, class C>
+__global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   typedef typename T::storage S;
-  constexpr int BK = Tile<T>::BK;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   S* As = reinterpret_cast<S*>(smem_raw);
-  S* Bs = As + 2 * Tile<T>::A_ELEMS;
-  __shared__ int64_t tgt_s[BM];
+  S* Bs = As + 2 * Lds<T, C>::A_ELEMS;
+  __shared__ int64_t tgt_s[C::BM];
 
-  const int tiles_m = (a.rows + BM - 1) / BM;
-  const int tiles_n = (int)((a.V + BN - 1) / BN);
+  const int tiles_m = (a.rows + C::BM - 1) / C::BM;
+  const int tiles_n = (int)((a.V + C::BN - 1) / C::BN);
   const int lin = xcd_remap(blockIdx.x, tiles_m * tiles_n);
   const int tm = lin % tiles_m, tn = lin / tiles_m;  // M fastest: blocks sharing a W tile are adjacent
-  const int m0 = tm * BM;
-  const int64_t n0 = (int64_t)tn * BN;
+  const int m0 = tm * C::BM;
+  const int64_t n0 = (int64_t)tn * C::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
   const S* X = static_cast<const S*>(a.X);
   const S* W = static_cast<const S*>(a.W);
-  for (int m = tid; m < BM; m += NT) {
+  for (int m = tid; m < C::BM; m += C::NT) {
     const int gm = m0 + m;
     tgt_s[m] = gm < a.rows ? a.targets[a.idx[gm]] : -1;
   }
 
-  KRowsLoader<T, BM> la;
-  KRowsLoader<T, BN> lb;
-  la.init(tid, [&](int r) -> const S* {
+  // X: gathered rows anywhere in [BT, H]; W: this tile's rows [n0, n0 + BN).
+  const uint32_t row_bytes = (uint32_t)a.H * (uint32_t)sizeof(S);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint64_t)a.BT * a.H * sizeof(S));
+  const int64_t nrows_w = a.V - n0 < C::BN ? a.V - n0 : C::BN;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + n0 * a.H, (uint64_t)nrows_w * a.H * sizeof(S));
+  KRowsLoader<T, C::BM, C::NT> la;
+  KRowsLoader<T, C::BN, C::NT> lb;
+  la.init(tid, [&](int r) -> uint32_t {
     const int gm = m0 + r;
-    return gm < a.rows ? X + (int64_t)a.idx[gm] * a.H : nullptr;
+    return gm < a.rows ? (uint32_t)a.idx[gm] * row_bytes : kOOB;
   });
-  lb.init(tid, [&](int r) -> const S* {
-    const int64_t gn = n0 + r;
-    return gn < a.V ? W + gn * a.H : nullptr;
-  });
+  lb.init(tid, [&](int r) -> uint32_t { return r < nrows_w ? (uint32_t)r * row_bytes : kOOB; });
 
-  f32x16_t acc[FM][FN];
-  zero_acc(acc);
+  f32x16_t acc[C::FM][C::FN];
+  zero_acc<C>(acc);
   const int K = (int)a.H;
-  const int nk = (K + BK - 1) / BK;
-  la.load(0, K);
-  lb.load(0, K);
-  la.store(As);
-  lb.store(Bs);
-  __syncthreads();
-  for (int t = 0; t < nk; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < nk) {
-      la.load((t + 1) * BK, K);
-      lb.load((t + 1) * BK, K);
-    }
-    mma_tile<T>(As + cur * Tile<T>::A_ELEMS, Bs + cur * Tile<T>::B_ELEMS, wm, wn, lane, acc);
-    if (t + 1 < nk) {
-      la.store(As + (cur ^ 1) * Tile<T>::A_ELEMS);
-      lb.store(Bs + (cur ^ 1) * Tile<T>::B_ELEMS);
-    }
-    __syncthreads();
-  }
+  main_loop<T, C>(
+      la, lb, [&](int k0) { la.load(xr, k0, K); }, [&](int k0) { lb.load(wr, k0, K); },
+      (K + KT<T>::BK - 1) / KT<T>::BK, As, Bs, wm, wn, lane, acc);
 
-  // Epilogue.
+  // Epilogue: store the logits, and per (row, 64-column block) the max and
+  // the sum of exp(z - max) in fp32.  Both tile shapes reduce a 64-column
+  // block the same way (8 lanes x 8 values), so a row's log-sum-exp does not
+  // depend on the chunking.
   S* slab = static_cast<S*>(a.slab);
-  const int64_t nblk0 = n0 + wn * WTN;  // first column of this wave's 64-column block
-  const bool blk_live = nblk0 < a.V;
-  const int64_t sidx = nblk0 / WTN;
+  float2* stats = reinterpret_cast<float2*>(a.stats);
+  staged_epilogue<C>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
+                     [&](int brow, int bcol, float (&v)[8]) {
+    const int gm = m0 + brow;
+    const int64_t gn = n0 + bcol;
+    float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int e = 0; e < 8; ++e)
+      if (gn + e < a.V) mx = fmaxf(mx, v[e]);
+    mx = group8_max(mx);
+    float se = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = acc_row(wm, i, r, lane);
-      const int gm = m0 + m;
-      float mx = -INFINITY;
+    for (int e = 0; e < 8; ++e)
+      if (gn + e < a.V) se += __expf(v[e] - mx);
+    se = group8_sum(se);
+    if (gm >= a.rows || gn >= a.V) return;
+    if ((bcol & 63) == 0) stats[(int64_t)gm * a.stats_ld + gn / 64] = float2{mx, se};
+    store8<T>(slab + (int64_t)gm * a.ldz + gn, v);
+    const int64_t tg = tgt_s[brow];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int64_t gn = n0 + acc_col(wn, j, lane);
-        if (gn < a.V) mx = fmaxf(mx, acc[i][j][r]);
-      }
-      mx = half_wave_max(mx);
-      float se = 0.f;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int64_t gn = n0 + acc_col(wn, j, lane);
-        if (gn < a.V) se += __expf(acc[i][j][r] - mx);
-      }
-      se = half_wave_sum(se);
-      if (gm < a.rows) {
-        if ((lane & 31) == 0 && blk_live) {
-          float2 st;
-          st.x = mx;
-          st.y = se;
-          reinterpret_cast<float2*>(a.stats)[(int64_t)gm * a.stats_ld + sidx] = st;
-        }
-        const int64_t tg = tgt_s[m];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int64_t gn = n0 + acc_col(wn, j, lane);
-          if (gn < a.V) {
-            slab[(int64_t)gm * a.ldz + gn] = T::from_f32(acc[i][j][r]);
-            if (gn == tg) a.ztgt[gm] = acc[i][j][r];
-          }
-        }
-      }
-    }
-  }
+    for (int e = 0; e < 8; ++e)
+      if (gn + e == tg) a.ztgt[gm] = v[e];
+  });
 }
 
 // ---------------------------------------------------------------------------
 // grad_input: dX[idx[m], n] = s * sum_k G[m, k] W[k, n] over one split of k,
 // or, with splits > 1, fp32 partials part[split][m][n] reduced afterwards.
 // ---------------------------------------------------------------------------
-template <class T>
-__global__ __launch_bounds__(NT) void dx_kernel(DxArgs a) {
+template <class T, class C>
+__global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
   typedef typename T::storage S;
-  constexpr int BK = Tile<T>::BK;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   S* As = reinterpret_cast<S*>(smem_raw);
-  S* Bs = As + 2 * Tile<T>::A_ELEMS;
+  S* Bs = As + 2 * Lds<T, C>::A_ELEMS;
 
-  const int tiles_m = (a.rows + BM - 1) / BM;
-  const int tiles_n = (int)((a.H + BN - 1) / BN);
+  const int tiles_m = (a.rows + C::BM - 1) / C::BM;
+  const int tiles_n = (int)((a.H + C::BN - 1) / C::BN);
   const int per_split = tiles_m * tiles_n;
   const int lin = xcd_remap(blockIdx.x, per_split * a.splits);
   const int split = lin / per_split;
   const int rem = lin % per_split;
   const int tm = rem % tiles_m, tn = rem / tiles_m;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
   const int64_t kbeg = (int64_t)split * a.k_per_split;
   const int64_t kend = kbeg + a.k_per_split < a.ldz ? kbeg + a.k_per_split : a.ldz;
@@ -357,74 +473,53 @@ __global__ __launch_bounds__(NT) void dx_kernel(DxArgs a) {
   const S* W = static_cast<const S*>(a.W);
   const int H = (int)a.H;
 
-  KRowsLoader<T, BM> la;
-  KColsLoader<T, BN> lb;
-  la.init(tid, [&](int r) -> const S* {
-    const int gm = m0 + r;
-    return gm < a.rows ? G + (int64_t)gm * a.ldz + kbeg : nullptr;
-  });
+  // G: this tile's rows [m0, m0 + BM) of the slab from column kbeg on;
+  // W: rows [kbeg, kend_w), one descriptor per k-tile.
+  const uint32_t gz_bytes = (uint32_t)a.ldz * (uint32_t)sizeof(S);
+  const int g_rows = a.rows - m0 < C::BM ? a.rows - m0 : C::BM;
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(
+      G + (int64_t)m0 * a.ldz + kbeg, ((uint64_t)g_rows * a.ldz - kbeg) * sizeof(S));
+  const uint32_t w_row_bytes = (uint32_t)H * (uint32_t)sizeof(S);
+  KRowsLoader<T, C::BM, C::NT> la;
+  KColsLoader<T, C::BN, C::NT> lb;
+  la.init(tid, [&](int r) -> uint32_t { return r < g_rows ? (uint32_t)r * gz_bytes : kOOB; });
   lb.init(tid);
-  auto wrow = [&](int k) -> const S* {
-    const int64_t gk = kbeg + k;
-    return gk < kend_w ? W + gk * H : nullptr;
-  };
 
-  f32x16_t acc[FM][FN];
-  zero_acc(acc);
+  f32x16_t acc[C::FM][C::FN];
+  zero_acc<C>(acc);
   const int K = (int)(kend - kbeg);
-  const int nk = (K + BK - 1) / BK;
-  if (nk > 0) {
-    la.load(0, K);
-    lb.load(0, wrow, n0, H);
-    la.store(As);
-    lb.store(Bs);
-    __syncthreads();
-    for (int t = 0; t < nk; ++t) {
-      const int cur = t & 1;
-      if (t + 1 < nk) {
-        la.load((t + 1) * BK, K);
-        lb.load((t + 1) * BK, wrow, n0, H);
-      }
-      mma_tile<T>(As + cur * Tile<T>::A_ELEMS, Bs + cur * Tile<T>::B_ELEMS, wm, wn, lane, acc);
-      if (t + 1 < nk) {
-        la.store(As + (cur ^ 1) * Tile<T>::A_ELEMS);
-        lb.store(Bs + (cur ^ 1) * Tile<T>::B_ELEMS);
-      }
-      __syncthreads();
-    }
-  }
+  main_loop<T, C>(
+      la, lb, [&](int k0) { la.load(gr, k0, K); },
+      [&](int k0) {
+        // W rows of this k-tile: one descriptor per tile keeps offsets small.
+        const int64_t r0 = kbeg + k0;
+        const int64_t nr = kend_w - r0 < KT<T>::BK ? kend_w - r0 : KT<T>::BK;
+        const __amdgpu_buffer_rsrc_t wr =
+            make_rsrc(W + r0 * H, nr > 0 ? (uint64_t)nr * H * sizeof(S) : 0);
+        lb.load(wr, 0, [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * w_row_bytes : kOOB; },
+                n0, H);
+      },
+      K > 0 ? (K + KT<T>::BK - 1) / KT<T>::BK : 0, As, Bs, wm, wn, lane, acc);
 
-  if (a.splits == 1) {
-    const float s = upstream_scale(a.grad_output, a.inv_n, a.reduction);
-    S* dX = static_cast<S*>(a.dX);
+  const float sc = upstream_scale(a.grad_output, a.inv_n, a.reduction);
+  S* dX = static_cast<S*>(a.dX);
+  float* part = a.partial + (int64_t)split * a.rows_cap * H;
+  const bool direct = a.splits == 1;
+  staged_epilogue<C>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
+                     [&](int brow, int bcol, float (&v)[8]) {
+    const int gm = m0 + brow;
+    const int gn = n0 + bcol;
+    if (gm >= a.rows || gn >= H) return;
+    if (direct) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gm = m0 + acc_row(wm, i, r, lane);
-        if (gm >= a.rows) continue;
-        const int64_t orow = (int64_t)a.idx[gm] * H;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int gn = n0 + acc_col(wn, j, lane);
-          if (gn < H) dX[orow + gn] = T::from_f32(s * acc[i][j][r]);
-        }
-      }
-  } else {
-    float* part = a.partial + (int64_t)split * a.rows_cap * H;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gm = m0 + acc_row(wm, i, r, lane);
-        if (gm >= a.rows) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int gn = n0 + acc_col(wn, j, lane);
-          if (gn < H) part[(int64_t)gm * H + gn] = acc[i][j][r];
-        }
-      }
-  }
+      for (int e = 0; e < 8; ++e) v[e] *= sc;
+      store8<T>(dX + (int64_t)a.idx[gm] * H + gn, v);
+    } else {
+      float* p = part + (int64_t)gm * H + gn;
+      *reinterpret_cast<f32x4_t*>(p) = f32x4_t{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4_t*>(p + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+    }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -432,132 +527,170 @@ __global__ __launch_bounds__(NT) void dx_kernel(DxArgs a) {
 // The accumulator starts at zero and the destination is read only in the
 // epilogue, so no [V, H] temporary exists.
 // ---------------------------------------------------------------------------
-template <class T>
-__global__ __launch_bounds__(NT) void dw_kernel(DwArgs a) {
+// Read-modify-write of 8 consecutive dW entries in the destination dtype D
+// (float, or the 16-bit operand type).
+template <class D>
+__device__ __forceinline__ void rmw8(void* dW, int64_t o, float (&v)[8], bool accumulate) {
+  if constexpr (std::is_same<D, float>::value) {
+    f32x4_t* p = reinterpret_cast<f32x4_t*>(static_cast<float*>(dW) + o);
+    f32x4_t lo{v[0], v[1], v[2], v[3]}, hi{v[4], v[5], v[6], v[7]};
+    if (accumulate) {
+      lo += p[0];
+      hi += p[1];
+    }
+    p[0] = lo;
+    p[1] = hi;
+  } else {
+    u32x4_t* p = reinterpret_cast<u32x4_t*>(static_cast<u16*>(dW) + o);
+    if (accumulate) {
+      float old[8];
+      unpack8<D>(*p, old);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += old[e];
+    }
+    *p = pack8<D>(v);
+  }
+}
+
+template <class T, class C, class D>
+__global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
   typedef typename T::storage S;
-  constexpr int BK = Tile<T>::BK;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   S* As = reinterpret_cast<S*>(smem_raw);
-  S* Bs = As + 2 * Tile<T>::A_ELEMS;
+  S* Bs = As + 2 * Lds<T, C>::A_ELEMS;
 
-  const int tiles_m = (int)((a.V + BM - 1) / BM);
-  const int tiles_n = (int)((a.H + BN - 1) / BN);
+  const int tiles_m = (int)((a.V + C::BM - 1) / C::BM);
+  const int tiles_n = (int)((a.H + C::BN - 1) / C::BN);
   const int lin = xcd_remap(blockIdx.x, tiles_m * tiles_n);
   const int tn = lin % tiles_n, tm = lin / tiles_n;  // N fastest: blocks sharing a G tile are adjacent
-  const int64_t m0 = (int64_t)tm * BM;
-  const int n0 = tn * BN;
+  const int64_t m0 = (int64_t)tm * C::BM;
+  const int n0 = tn * C::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int H = (int)a.H;
 
   const S* G = static_cast<const S*>(a.slab);
   const S* X = static_cast<const S*>(a.X);
-  KColsLoader<T, BM> la;
-  KColsLoader<T, BN> lb;
+  // G: the chunk's rows (k) of the slab, one descriptor per k-tile; X:
+  // gathered rows anywhere in [BT, H].
+  const uint32_t gz_bytes = (uint32_t)a.ldz * (uint32_t)sizeof(S);
+  const uint32_t x_row_bytes = (uint32_t)H * (uint32_t)sizeof(S);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint64_t)a.BT * H * sizeof(S));
+  KColsLoader<T, C::BM, C::NT> la;
+  KColsLoader<T, C::BN, C::NT> lb;
   la.init(tid);
   lb.init(tid);
-  auto grow = [&](int k) -> const S* { return k < a.rows ? G + (int64_t)k * a.ldz : nullptr; };
-  auto xrow = [&](int k) -> const S* {
-    return k < a.rows ? X + (int64_t)a.idx[k] * H : nullptr;
+  auto xrow = [&](int k) -> uint32_t {
+    return k < a.rows ? (uint32_t)a.idx[k] * x_row_bytes : kOOB;
   };
   const int ldz_cols = (int)a.ldz;
 
-  f32x16_t acc[FM][FN];
-  zero_acc(acc);
-  const int nk = (a.rows + BK - 1) / BK;
-  la.load(0, grow, (int)m0, ldz_cols);
-  lb.load(0, xrow, n0, H);
-  la.store(As);
-  lb.store(Bs);
-  __syncthreads();
-  for (int t = 0; t < nk; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < nk) {
-      la.load((t + 1) * BK, grow, (int)m0, ldz_cols);
-      lb.load((t + 1) * BK, xrow, n0, H);
-    }
-    mma_tile<T>(As + cur * Tile<T>::A_ELEMS, Bs + cur * Tile<T>::B_ELEMS, wm, wn, lane, acc);
-    if (t + 1 < nk) {
-      la.store(As + (cur ^ 1) * Tile<T>::A_ELEMS);
-      lb.store(Bs + (cur ^ 1) * Tile<T>::B_ELEMS);
-    }
-    __syncthreads();
-  }
+  f32x16_t acc[C::FM][C::FN];
+  zero_acc<C>(acc);
+  main_loop<T, C>(
+      la, lb,
+      [&](int k0) {
+        const int nr = a.rows - k0 < KT<T>::BK ? a.rows - k0 : KT<T>::BK;
+        const __amdgpu_buffer_rsrc_t gr =
+            make_rsrc(G + (int64_t)k0 * a.ldz, nr > 0 ? (uint64_t)nr * a.ldz * sizeof(S) : 0);
+        la.load(gr, 0, [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * gz_bytes : kOOB; },
+                (int)m0, ldz_cols);
+      },
+      [&](int k0) { lb.load(xr, k0, xrow, n0, H); }, (a.rows + KT<T>::BK - 1) / KT<T>::BK, As, Bs,
+      wm, wn, lane, acc);
 
-  const float s = upstream_scale(a.grad_output, a.inv_n, a.reduction);
+  const float sc = upstream_scale(a.grad_output, a.inv_n, a.reduction);
+  const bool accumulate = a.accumulate != 0;
+  staged_epilogue<C>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
+                     [&](int brow, int bcol, float (&v)[8]) {
+    const int64_t gm = m0 + brow;
+    const int gn = n0 + bcol;
+    if (gm >= a.V || gn >= H) return;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t gm = m0 + acc_row(wm, i, r, lane);
-      if (gm >= a.V) continue;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int gn = n0 + acc_col(wn, j, lane);
-        if (gn >= H) continue;
-        const int64_t o = gm * H + gn;
-        float v = s * acc[i][j][r];
-        if (a.accumulate) v += load_as(a.dW, o, a.dw_dtype);
-        store_as(a.dW, o, v, a.dw_dtype);
-      }
-    }
+    for (int e = 0; e < 8; ++e) v[e] *= sc;
+    rmw8<D>(a.dW, gm * H + gn, v, accumulate);
+  });
 }
 
 // ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
-// The 72 KiB of LDS per workgroup is above the default dynamic limit; raise
-// the limit once per kernel (gfx950 has 160 KiB of LDS per CU).
+// Workgroups above 64 KiB of LDS need the per-kernel limit raised (gfx950 has
+// 160 KiB per CU).  Done once per kernel instantiation.
 template <class K>
 static hipError_t allow_lds(K kernel, size_t bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <class T>
+template <class T, class C>
 static hipError_t launch_logits_t(const LogitsArgs& a, hipStream_t st) {
-  static const hipError_t prep = allow_lds(logits_kernel<T>, Tile<T>::LDS_BYTES);
+  static const hipError_t prep = allow_lds(logits_kernel<T, C>, Lds<T, C>::BYTES);
   if (prep != hipSuccess) return prep;
-  const int tiles = ((a.rows + BM - 1) / BM) * (int)((a.V + BN - 1) / BN);
-  hipLaunchKernelGGL(logits_kernel<T>, dim3(tiles), dim3(NT), Tile<T>::LDS_BYTES, st, a);
+  const int tiles = ((a.rows + C::BM - 1) / C::BM) * (int)((a.V + C::BN - 1) / C::BN);
+  logits_kernel<T, C><<<dim3(tiles), dim3(C::NT), Lds<T, C>::BYTES, st>>>(a);
   return hipGetLastError();
 }
-template <class T>
+template <class T, class C>
 static hipError_t launch_dx_t(const DxArgs& a, hipStream_t st) {
-  static const hipError_t prep = allow_lds(dx_kernel<T>, Tile<T>::LDS_BYTES);
+  static const hipError_t prep = allow_lds(dx_kernel<T, C>, Lds<T, C>::BYTES);
   if (prep != hipSuccess) return prep;
-  const int tiles = ((a.rows + BM - 1) / BM) * (int)((a.H + BN - 1) / BN) * a.splits;
-  hipLaunchKernelGGL(dx_kernel<T>, dim3(tiles), dim3(NT), Tile<T>::LDS_BYTES, st, a);
+  const int tiles = ((a.rows + C::BM - 1) / C::BM) * (int)((a.H + C::BN - 1) / C::BN) * a.splits;
+  dx_kernel<T, C><<<dim3(tiles), dim3(C::NT), Lds<T, C>::BYTES, st>>>(a);
   return hipGetLastError();
 }
-template <class T>
+template <class T, class C, class D>
 static hipError_t launch_dw_t(const DwArgs& a, hipStream_t st) {
-  static const hipError_t prep = allow_lds(dw_kernel<T>, Tile<T>::LDS_BYTES);
+  static const hipError_t prep = allow_lds(dw_kernel<T, C, D>, Lds<T, C>::BYTES);
   if (prep != hipSuccess) return prep;
-  const int tiles = (int)((a.V + BM - 1) / BM) * (int)((a.H + BN - 1) / BN);
-  hipLaunchKernelGGL(dw_kernel<T>, dim3(tiles), dim3(NT), Tile<T>::LDS_BYTES, st, a);
+  const int tiles = (int)((a.V + C::BM - 1) / C::BM) * (int)((a.H + C::BN - 1) / C::BN);
+  dw_kernel<T, C, D><<<dim3(tiles), dim3(C::NT), Lds<T, C>::BYTES, st>>>(a);
   return hipGetLastError();
+}
+
+// Tile choice.  The big tile needs enough rows and columns to fill it; the
+// grad_weight update with few rows per chunk is bound by the dW
+// read-modify-write, where two resident workgroups per CU hide more latency.
+bool logits_big(int rows, int64_t V) { return rows > 128 && V >= 1024; }
+bool dx_big(int rows, int64_t H) { return rows > 128 && H >= 256; }
+bool dw_big(int rows, int64_t H) { return rows > 512 && H >= 256; }
+
+template <class T>
+static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
+  return logits_big(a.rows, a.V) ? launch_logits_t<T, Big>(a, st) : launch_logits_t<T, Small>(a, st);
+}
+template <class T>
+static hipError_t dx_t(const DxArgs& a, hipStream_t st) {
+  return dx_big(a.rows, a.H) ? launch_dx_t<T, Big>(a, st) : launch_dx_t<T, Small>(a, st);
+}
+template <class T, class D>
+static hipError_t dw_t(const DwArgs& a, hipStream_t st) {
+  return dw_big(a.rows, a.H) ? launch_dw_t<T, Big, D>(a, st) : launch_dw_t<T, Small, D>(a, st);
 }
 
 hipError_t launch_logits(int dtype, const LogitsArgs& a, hipStream_t st) {
-  if (dtype == 0) return launch_logits_t<F32>(a, st);
-  if (dtype == 1) return launch_logits_t<F16>(a, st);
-  return launch_logits_t<BF16>(a, st);
+  if (dtype == 0) return logits_t<F32>(a, st);
+  if (dtype == 1) return logits_t<F16>(a, st);
+  return logits_t<BF16>(a, st);
 }
 hipError_t launch_dx(int dtype, const DxArgs& a, hipStream_t st) {
-  if (dtype == 0) return launch_dx_t<F32>(a, st);
-  if (dtype == 1) return launch_dx_t<F16>(a, st);
-  return launch_dx_t<BF16>(a, st);
+  if (dtype == 0) return dx_t<F32>(a, st);
+  if (dtype == 1) return dx_t<F16>(a, st);
+  return dx_t<BF16>(a, st);
 }
 hipError_t launch_dw(int dtype, const DwArgs& a, hipStream_t st) {
-  if (dtype == 0) return launch_dw_t<F32>(a, st);
-  if (dtype == 1) return launch_dw_t<F16>(a, st);
-  return launch_dw_t<BF16>(a, st);
+  // dW is fp32 or the operand dtype.
+  if (dtype == 0) return dw_t<F32, float>(a, st);
+  if (dtype == 1) return a.dw_dtype == 0 ? dw_t<F16, float>(a, st) : dw_t<F16, F16>(a, st);
+  return a.dw_dtype == 0 ? dw_t<BF16, float>(a, st) : dw_t<BF16, BF16>(a, st);
 }
 
-int gemm_bk(int dtype) { return dtype == 0 ? Tile<F32>::BK : Tile<BF16>::BK; }
-int stats_cols_per_block() { return WTN; }
-int gemm_block_m() { return BM; }
-int gemm_block_n() { return BN; }
+int dx_tile_m(int rows, int64_t H) { return dx_big(rows, H) ? Big::BM : Small::BM; }
+int dx_tile_n(int rows, int64_t H) { return dx_big(rows, H) ? Big::BN : Small::BN; }
+// Column width of one (max, sum exp) entry written by the logits GEMM.
+int stats_cols() {
+  static_assert(Big::FN % 2 == 0 && Small::FN % 2 == 0, "64-column stats blocks");
+  return 64;
+}
 
 }  // namespace flce

@@ -12,7 +12,7 @@ struct LogitsArgs {
   const int32_t* idx;      // [rows] labelled row ids of this chunk
   const int64_t* targets;  // [BT]
   int rows;
-  int64_t H, V;
+  int64_t BT, H, V;
   void* slab;              // [rows_cap, ldz] operand dtype
   int64_t ldz;
   float* stats;            // [rows_cap, stats_ld] float2 (max, sum exp) per 64-column block
@@ -71,7 +71,7 @@ struct DwArgs {
   const void* X;     // [BT, H]
   const int32_t* idx;
   int rows;
-  int64_t H, V, ldz;
+  int64_t BT, H, V, ldz;
   void* dW;          // [V, H] dw_dtype
   int dw_dtype;      // 0 f32, 1 f16, 2 bf16
   int accumulate;    // 1: add to dW
@@ -101,9 +101,8 @@ hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st);
 hipError_t launch_scale_cast(const void* src, int src_dtype, void* dst, int dst_dtype,
                              int64_t n, const float* scale, hipStream_t st);
 
-int gemm_bk(int dtype);
-int stats_cols_per_block();
-int gemm_block_m();
-int gemm_block_n();
+int dx_tile_m(int rows, int64_t H);
+int dx_tile_n(int rows, int64_t H);
+int stats_cols();
 
 }  // namespace flce
