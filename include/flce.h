@@ -177,7 +177,8 @@ typedef enum {
   FLCE_K_DW = 6,          /* grad_weight GEMM written into dW                         */
   FLCE_K_FINALIZE = 7,    /* loss reduction                                           */
   FLCE_K_FILL = 8,        /* zero-fill / cast helpers                                 */
-  FLCE_K_COUNT = 9
+  FLCE_K_GATHER = 9,      /* gather of the chunk's labelled X rows (transposed)       */
+  FLCE_K_COUNT = 10
 } flce_kernel_kind_t;
 
 typedef struct {

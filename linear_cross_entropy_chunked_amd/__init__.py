@@ -22,7 +22,7 @@ REDUCTIONS = {"mean": MEAN, "sum": SUM, "none": NONE}
 STATUS = {0: "FLCE_OK", -1: "FLCE_E_ARG", -2: "FLCE_E_DTYPE", -3: "FLCE_E_TARGET",
           -4: "FLCE_E_WORKSPACE", -5: "FLCE_E_HIP"}
 KERNEL_KINDS = ["mask_scan", "zero_ignored_rows", "logits_gemm", "softmax_grad", "dx_gemm",
-                "dx_reduce", "dw_gemm", "loss_finalize", "fill_cast"]
+                "dx_reduce", "dw_gemm", "loss_finalize", "fill_cast", "gather_rows"]
 
 # Every symbol include/flce.h declares.
 EXPORTS = ["flce_chunk_size", "flce_workspace_bytes", "flce_fwd_bwd", "flce_scale_cast",
@@ -49,7 +49,7 @@ class FlceStats(ctypes.Structure):
 
 
 class FlceProfile(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int64 * 9), ("total_ms", ctypes.c_double * 9)]
+    _fields_ = [("launches", ctypes.c_int64 * 10), ("total_ms", ctypes.c_double * 10)]
 
 
 _lib = None
@@ -132,7 +132,8 @@ def flce_profile_end() -> dict:
     rc = load().flce_profile_end(ctypes.byref(p))
     if rc != 0:
         raise FlceError(rc, "flce_profile_end")
-    return {KERNEL_KINDS[k]: (int(p.launches[k]), float(p.total_ms[k])) for k in range(9)}
+    return {KERNEL_KINDS[k]: (int(p.launches[k]), float(p.total_ms[k]))
+            for k in range(len(KERNEL_KINDS))}
 
 
 def flce_kernel_name(kind: int) -> str:

@@ -54,11 +54,11 @@ constexpr int64_t kDxMinKPerSplit = 1024;
 constexpr int kDxMaxSplits = 32;
 
 struct Layout {
-  int64_t c = 0, ldz = 0, stats_ld = 0;
+  int64_t c = 0, ldz = 0, ldx = 0, stats_ld = 0;
   int splits = 1;
   int64_t k_per_split = 0;
-  size_t off_slab = 0, off_stats = 0, off_ztgt = 0, off_partial = 0, off_idx = 0, off_lossrow = 0,
-         off_flags = 0, total = 0;
+  size_t off_slab = 0, off_xct = 0, off_stats = 0, off_ztgt = 0, off_partial = 0, off_idx = 0,
+         off_lossrow = 0, off_flags = 0, total = 0;
 };
 
 size_t itemsize(int dt) { return dt == FLCE_F32 ? 4 : 2; }
@@ -67,6 +67,7 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t c) {
   Layout L;
   L.c = c;
   L.ldz = round_up(V, 8);
+  L.ldx = round_up(c, 8);
   L.stats_ld = ceil_div(V, stats_cols());
   const int64_t tiles = ceil_div(c, dx_tile_m((int)c, H)) * ceil_div(H, dx_tile_n((int)c, H));
   int64_t splits = ceil_div(kDxTargetBlocks, tiles);
@@ -83,6 +84,7 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t c) {
     return o;
   };
   L.off_slab = take((size_t)c * L.ldz * itemsize(dtype));
+  L.off_xct = take((size_t)H * L.ldx * itemsize(dtype));
   L.off_stats = take((size_t)c * L.stats_ld * 8);
   L.off_ztgt = take((size_t)c * 4);
   L.off_partial = take(L.splits > 1 ? (size_t)L.splits * c * H * 4 : 0);
@@ -192,9 +194,9 @@ const char* flce_status_string(int status) {
 const char* flce_last_error(void) { return g_last_error; }
 
 const char* flce_kernel_name(int kind) {
-  static const char* names[FLCE_K_COUNT] = {"mask_scan",  "zero_ignored_rows", "logits_gemm",
-                                            "softmax_grad", "dx_gemm",         "dx_reduce",
-                                            "dw_gemm",    "loss_finalize",     "fill_cast"};
+  static const char* names[FLCE_K_COUNT] = {
+      "mask_scan", "zero_ignored_rows", "logits_gemm", "softmax_grad", "dx_gemm",
+      "dx_reduce", "dw_gemm",           "loss_finalize", "fill_cast",  "gather_rows"};
   return (kind >= 0 && kind < FLCE_K_COUNT) ? names[kind] : "unknown";
 }
 
@@ -277,6 +279,7 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
   const int dw_dt = (int)accum_dtype;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   void* slab = ws + L.off_slab;
+  void* xct = ws + L.off_xct;
   float* stats_buf = reinterpret_cast<float*>(ws + L.off_stats);
   float* ztgt = reinterpret_cast<float*>(ws + L.off_ztgt);
   float* partial = reinterpret_cast<float*>(ws + L.off_partial);
@@ -408,15 +411,15 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
     }
 
     if (!frozen_weight) {
+      FLCE_LAUNCH(FLCE_K_GATHER, launch_gather_t(dt, X, cidx, rows, H, xct, L.ldx, st));
       DwArgs wa;
       wa.slab = slab;
-      wa.X = X;
-      wa.idx = cidx;
+      wa.XcT = xct;
       wa.rows = rows;
-      wa.BT = BT;
       wa.H = H;
       wa.V = V;
       wa.ldz = L.ldz;
+      wa.ldx = L.ldx;
       wa.dW = dW;
       wa.dw_dtype = dw_dt;
       wa.accumulate = (accumulate_dw || k > 0) ? 1 : 0;

@@ -570,19 +570,18 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
   const int H = (int)a.H;
 
   const S* G = static_cast<const S*>(a.slab);
-  const S* X = static_cast<const S*>(a.X);
-  // G: the chunk's rows (k) of the slab, one descriptor per k-tile; X:
-  // gathered rows anywhere in [BT, H].
+  const S* XcT = static_cast<const S*>(a.XcT);
+  // G: the chunk's rows (k) of the slab, one descriptor per k-tile; XcT:
+  // hidden units [n0, n0 + BN) of the gathered chunk, k contiguous.
   const uint32_t gz_bytes = (uint32_t)a.ldz * (uint32_t)sizeof(S);
-  const uint32_t x_row_bytes = (uint32_t)H * (uint32_t)sizeof(S);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint64_t)a.BT * H * sizeof(S));
+  const uint32_t xt_row_bytes = (uint32_t)a.ldx * (uint32_t)sizeof(S);
+  const int xt_rows = H - n0 < C::BN ? H - n0 : C::BN;
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(XcT + (int64_t)n0 * a.ldx, (uint64_t)xt_rows * a.ldx * sizeof(S));
   KColsLoader<T, C::BM, C::NT> la;
-  KColsLoader<T, C::BN, C::NT> lb;
+  KRowsLoader<T, C::BN, C::NT> lb;
   la.init(tid);
-  lb.init(tid);
-  auto xrow = [&](int k) -> uint32_t {
-    return k < a.rows ? (uint32_t)a.idx[k] * x_row_bytes : kOOB;
-  };
+  lb.init(tid, [&](int r) -> uint32_t { return r < xt_rows ? (uint32_t)r * xt_row_bytes : kOOB; });
   const int ldz_cols = (int)a.ldz;
 
   f32x16_t acc[C::FM][C::FN];
@@ -596,7 +595,7 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
         la.load(gr, 0, [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * gz_bytes : kOOB; },
                 (int)m0, ldz_cols);
       },
-      [&](int k0) { lb.load(xr, k0, xrow, n0, H); }, (a.rows + KT<T>::BK - 1) / KT<T>::BK, As, Bs,
+      [&](int k0) { lb.load(xr, k0, a.rows); }, (a.rows + KT<T>::BK - 1) / KT<T>::BK, As, Bs,
       wm, wn, lane, acc);
 
   const float sc = upstream_scale(a.grad_output, a.inv_n, a.reduction);

@@ -68,10 +68,9 @@ struct DxReduceArgs {
 // grad_weight GEMM of one chunk.
 struct DwArgs {
   const void* slab;  // G [rows, ldz]
-  const void* X;     // [BT, H]
-  const int32_t* idx;
+  const void* XcT;   // [H, ldx] the chunk's gathered rows, transposed
   int rows;
-  int64_t BT, H, V, ldz;
+  int64_t H, V, ldz, ldx;
   void* dW;          // [V, H] dw_dtype
   int dw_dtype;      // 0 f32, 1 f16, 2 bf16
   int accumulate;    // 1: add to dW
@@ -93,6 +92,8 @@ hipError_t launch_softmax(int dtype, const SoftmaxArgs& a, hipStream_t st);
 hipError_t launch_dx_reduce(int dtype, const DxReduceArgs& a, hipStream_t st);
 hipError_t launch_mask_scan(const int64_t* targets, int64_t BT, int64_t V, int64_t ignore_index,
                             int32_t* idx, ScanFlags* flags, hipStream_t st);
+hipError_t launch_gather_t(int dtype, const void* X, const int32_t* idx, int rows, int64_t H,
+                           void* XcT, int64_t ldx, hipStream_t st);
 hipError_t launch_zero_ignored(const int64_t* targets, int64_t BT, int64_t H,
                                int64_t ignore_index, void* dX, int dx_dtype, float* loss_none,
                                hipStream_t st);

@@ -81,6 +81,55 @@ hipError_t launch_mask_scan(const int64_t* targets, int64_t BT, int64_t V, int64
 }
 
 // ---------------------------------------------------------------------------
+// Row gather of the chunk's labelled X rows, written transposed:
+// XcT[h, r] = X[idx[r], h] for r < rows, 0 for rows <= r < ldx (PR #1554,
+// Details item 3: the compacted rows of a chunk are gathered into one reused
+// chunk buffer).  The transposed layout makes the chunk's rows the contiguous
+// k dimension of the grad_weight GEMM.  64 x 64 tiles through LDS.
+// ---------------------------------------------------------------------------
+template <class S>
+__global__ __launch_bounds__(256) void gather_t_kernel(const S* __restrict__ X,
+                                                       const int32_t* __restrict__ idx, int rows,
+                                                       int64_t H, S* __restrict__ XcT,
+                                                       int64_t ldx) {
+  __shared__ S tile[64][65];
+  __shared__ int32_t ridx[64];
+  const int r0 = blockIdx.x * 64;
+  const int64_t h0 = (int64_t)blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  if (tid < 64) ridx[tid] = (r0 + tid < rows) ? idx[r0 + tid] : -1;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int q = tid + e * 256;
+    const int r = q >> 6, h = q & 63;
+    const int32_t src = ridx[r];
+    S v = S(0);
+    if (src >= 0 && h0 + h < H) v = X[(int64_t)src * H + h0 + h];
+    tile[r][h] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int q = tid + e * 256;
+    const int h = q >> 6, r = q & 63;
+    if (h0 + h < H && r0 + r < ldx) XcT[(h0 + h) * ldx + r0 + r] = tile[r][h];
+  }
+}
+
+hipError_t launch_gather_t(int dtype, const void* X, const int32_t* idx, int rows, int64_t H,
+                           void* XcT, int64_t ldx, hipStream_t st) {
+  const dim3 grid((unsigned)((ldx + 63) / 64), (unsigned)((H + 63) / 64));
+  if (dtype == 0)
+    hipLaunchKernelGGL(gather_t_kernel<float>, grid, dim3(256), 0, st,
+                       static_cast<const float*>(X), idx, rows, H, static_cast<float*>(XcT), ldx);
+  else
+    hipLaunchKernelGGL(gather_t_kernel<u16>, grid, dim3(256), 0, st, static_cast<const u16*>(X),
+                       idx, rows, H, static_cast<u16*>(XcT), ldx);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Ignored rows get a +0.0 grad_input row and +0.0 per-token loss (PR #1554,
 // Details item 1).  Labelled rows are left alone: the projections write them.
 // ---------------------------------------------------------------------------

@@ -42,7 +42,7 @@ def test_exported_symbols_in_dynamic_table(flce_lib):
 def test_status_and_kernel_names(flce_lib):
     assert flce_lib.flce_status_string(0) == "FLCE_OK"
     assert flce_lib.flce_status_string(-3).startswith("FLCE_E_TARGET")
-    assert [flce_lib.flce_kernel_name(k) for k in range(9)] == flce_lib.KERNEL_KINDS
+    assert [flce_lib.flce_kernel_name(k) for k in range(10)] == flce_lib.KERNEL_KINDS
 
 
 # ------------------------------------------------------------- chunk policy
