@@ -41,25 +41,15 @@ typedef Cfg<128, 128> Small;
 template <class T>
 struct KT {  // k-tile geometry per element type
   typedef typename T::storage S;
-  static constexpr int BK = (sizeof(S) == 2) ? 64 : 32;
-  static constexpr int LDK = BK + 16 / (int)sizeof(S);  // padded LDS row (elements)
-};
-
-template <class T, class C>
-struct Lds {
-  static constexpr int A_ELEMS = C::BM * KT<T>::LDK;
-  static constexpr int B_ELEMS = C::BN * KT<T>::LDK;
-  static constexpr size_t OPERANDS = 2 * (size_t)(A_ELEMS + B_ELEMS) * sizeof(typename T::storage);
-  // the epilogue stages WTM x (BN + 4) fp32 in the same memory
-  static constexpr size_t STAGE = (size_t)C::WTM * (C::BN + 4) * sizeof(float);
-  static constexpr size_t BYTES = OPERANDS > STAGE ? OPERANDS : STAGE;
+  static constexpr int BK = (sizeof(S) == 2) ? 64 : 32;  // 128 bytes of k per row
+  static constexpr int LDK = BK + 16 / (int)sizeof(S);  // padded row of the register path
+  static constexpr int RB = BK * (int)sizeof(S);          // bytes per row, swizzled layout
 };
 
 // ---------------------------------------------------------------------------
-// Operand tile loaders.  Each fills an R x BK tile of LDS laid out [R][LDK].
-// Global reads are raw buffer loads: a wave-uniform descriptor (base, byte
-// range) plus a 32-bit per-lane byte offset; any offset at or past the range
-// reads as zero, which is how rows and columns outside the problem are
+// Global memory access.  Raw buffer loads: a wave-uniform descriptor (base,
+// byte range) plus a 32-bit per-lane byte offset; any offset at or past the
+// range reads as zero, which is how rows and columns outside the problem are
 // masked (an out-of-range lane gets kOOB).
 // ---------------------------------------------------------------------------
 constexpr uint32_t kOOB = 0xfffffff0u;
@@ -72,66 +62,129 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
+// 16 bytes per lane straight into LDS: lane i of the wave writes lds + 16 i.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               unsigned char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
+}
 
-// Source already k-contiguous: tile row r starts at byte offset rowoff(r)
-// (kOOB: zero row) of the descriptor.  Vectors whose first k is >= kend read
-// as zero; callers keep kend a multiple of the vector width, and elements
-// between the logical K and kend are zero in memory.
-template <class T, int R, int NT>
-struct KRowsLoader {
+// Wait until at most `vm` vector-memory loads of this wave are outstanding
+// and all its LDS operations are done, then meet the other waves.  A plain
+// s_barrier: the workgroup fence of __syncthreads would also wait for the
+// loads still streaming into the other LDS buffer.
+template <int VM>
+__device__ __forceinline__ void wait_and_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  constexpr int imm = (VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(imm);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// LDS layouts of an R x BK operand tile (k contiguous within a row).
+//   Swz: rows of RB = 128 bytes, unpadded, 16-byte chunks XOR-swizzled by
+//        row: physical chunk p of row r holds k-chunk p ^ (r % 8).  Filled
+//        directly from global memory; 8 lanes reading one chunk of 8
+//        consecutive rows hit 8 distinct bank groups.
+//   Pad: rows of LDK elements (16-byte pad), filled from registers.
+// frag16: the 16 bytes of k-chunk kc of row r; frag4: element k of row r.
+// ---------------------------------------------------------------------------
+template <class T>
+struct Swz {
   typedef typename T::storage S;
-  static constexpr int BK = KT<T>::BK;
-  static constexpr int VPR = BK / T::vec;
-  static constexpr int NV = R * VPR / NT;
-  static_assert((R * VPR) % NT == 0, "tile not divisible among threads");
-  u32x4_t reg[NV];
-  uint32_t roff[NV];
-  int kofs[NV];
-  int lrow[NV];
-
-  template <class RowFn>
-  __device__ void init(int tid, RowFn rowoff) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int v = tid + i * NT;
-      lrow[i] = v / VPR;
-      kofs[i] = (v % VPR) * T::vec;
-      roff[i] = rowoff(lrow[i]);
-    }
+  static constexpr int RB = KT<T>::RB;
+  static_assert(RB == 128, "swizzle assumes 128-byte rows");
+  static constexpr size_t bytes(int R) { return (size_t)R * RB; }
+  __device__ static const unsigned char* chunk(const unsigned char* b, int r, int kc) {
+    return b + r * RB + ((kc ^ (r & 7)) << 4);
   }
-  __device__ void load(__amdgpu_buffer_rsrc_t rs, int k0, int kend) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int k = k0 + kofs[i];
-      const uint32_t off =
-          (roff[i] != kOOB && k < kend) ? roff[i] + (uint32_t)k * (uint32_t)sizeof(S) : kOOB;
-      reg[i] = buf_load16(rs, off);
-    }
+  __device__ static u32x4_t frag16(const unsigned char* b, int r, int kc) {
+    return *reinterpret_cast<const u32x4_t*>(chunk(b, r, kc));
   }
-  __device__ void store(S* lds) const {
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      *reinterpret_cast<u32x4_t*>(lds + lrow[i] * KT<T>::LDK + kofs[i]) = reg[i];
+  __device__ static float frag4(const unsigned char* b, int r, int k) {
+    return reinterpret_cast<const float*>(chunk(b, r, k >> 2))[k & 3];
+  }
+};
+template <class T>
+struct Pad {
+  typedef typename T::storage S;
+  static constexpr int LDK = KT<T>::LDK;
+  static constexpr size_t bytes(int R) { return (size_t)R * LDK * sizeof(S); }
+  __device__ static u32x4_t frag16(const unsigned char* b, int r, int kc) {
+    return *reinterpret_cast<const u32x4_t*>(b + (r * LDK) * sizeof(S) + kc * 16);
+  }
+  __device__ static float frag4(const unsigned char* b, int r, int k) {
+    return reinterpret_cast<const float*>(b)[r * LDK + k];
   }
 };
 
-// Source contiguous along the tile's row index: tile element (r, k) sits at
-// byte offset rowoff(k) + (c0 + r) * sizeof(S) of the descriptor, rowoff(k) ==
-// kOOB for a zero k-row; columns at or past cend read as zero (vector
-// granularity).  Each thread moves a TK x TK block (TK = elements per 16
-// bytes: 8 k-rows x 8 columns for 16-bit types, 4 x 4 for fp32) and
-// transposes it in registers.  Lane order is k-block fastest, so a wave's
-// global reads cover 128 contiguous bytes per row and its 16-byte LDS writes
-// fall in distinct banks.
+// ---------------------------------------------------------------------------
+// Operand tile loaders.
+// ---------------------------------------------------------------------------
+
+// k-contiguous source, straight into a Swz tile.  Tile row r starts at byte
+// offset rowoff(r) (kOOB: zero row) of the descriptor.  Each wave instruction
+// fills 8 rows (1 KiB): lane L takes row L / 8 of the group and physical chunk
+// L % 8, i.e. k-chunk (L % 8) ^ (L / 8).  Chunks whose first k is >= kend read
+// as zero; callers keep kend a multiple of the chunk width, and elements
+// between the logical K and kend are zero in memory.
+template <class T, int R, int NWAVES>
+struct DmaRows {
+  static constexpr bool kDirect = true;
+  typedef typename T::storage S;
+  static constexpr int RPI = 1024 / KT<T>::RB;  // rows per instruction
+  static constexpr int NI = R / RPI / NWAVES;    // instructions per wave per k-tile
+  static_assert(R % (RPI * NWAVES) == 0, "tile rows not divisible among waves");
+  static constexpr size_t TILE_BYTES = Swz<T>::bytes(R);
+  struct Regs {};
+  uint32_t roff[NI];
+  int kc_el;  // first k (elements) of this lane's chunk
+  int wave;
+
+  template <class RowFn>
+  __device__ void init(int tid, RowFn rowoff) {
+    const int lane = tid & 63;
+    wave = tid >> 6;
+    const int rin = lane / 8;
+    kc_el = ((lane & 7) ^ rin) * T::vec;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) roff[i] = rowoff((wave + i * NWAVES) * RPI + rin);
+  }
+  __device__ void dma(__amdgpu_buffer_rsrc_t rs, unsigned char* tile, int k0, int kend) const {
+    const int k = k0 + kc_el;
+    const bool kin = k < kend;
+    const uint32_t kb = (uint32_t)k * (uint32_t)sizeof(S);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      buf_load16_lds(rs, (kin && roff[i] != kOOB) ? roff[i] + kb : kOOB,
+                     tile + (wave + i * NWAVES) * 1024);
+  }
+};
+
+// Source contiguous along the tile's row index, into a Pad tile: tile element
+// (r, k) sits at byte offset rowoff(k) + (c0 + r) * sizeof(S) of the
+// descriptor, rowoff(k) == kOOB for a zero k-row; columns at or past cend
+// read as zero (vector granularity).  Each thread moves a TK x TK block (TK =
+// elements per 16 bytes: 8 k-rows x 8 columns for 16-bit types, 4 x 4 for
+// fp32) and transposes it in registers.  Lane order is k-block fastest, so a
+// wave's global reads cover 128 contiguous bytes per row and its 16-byte LDS
+// writes fall in distinct banks.
 template <class T, int R, int NT>
 struct KColsLoader {
+  static constexpr bool kDirect = false;
   typedef typename T::storage S;
   static constexpr int TK = T::vec;
   static constexpr int BK = KT<T>::BK;
   static constexpr int KBN = BK / TK;             // k blocks per tile
   static constexpr int NBLK = (R / TK) * KBN;     // blocks per tile
   static constexpr int NB = (NBLK + NT - 1) / NT; // blocks per thread
-  u32x4_t reg[NB][TK];
+  static constexpr size_t TILE_BYTES = Pad<T>::bytes(R);
+  struct Regs {
+    u32x4_t v[NB][TK];
+  };
   int cb[NB], kb[NB];
   bool act[NB];
 
@@ -145,7 +198,8 @@ struct KColsLoader {
     }
   }
   template <class KFn>
-  __device__ void load(__amdgpu_buffer_rsrc_t rs, int k0, KFn rowoff, int c0, int cend) {
+  __device__ void load(Regs& g, __amdgpu_buffer_rsrc_t rs, int k0, KFn rowoff, int c0,
+                       int cend) const {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int c = c0 + cb[i] * TK;
@@ -154,24 +208,25 @@ struct KColsLoader {
 #pragma unroll
       for (int q = 0; q < TK; ++q) {
         const uint32_t ro = rowoff(k0 + kb[i] * TK + q);
-        reg[i][q] = buf_load16(rs, (col_ok && ro != kOOB) ? ro + cofs : kOOB);
+        g.v[i][q] = buf_load16(rs, (col_ok && ro != kOOB) ? ro + cofs : kOOB);
       }
     }
   }
-  __device__ void store(S* lds) const {
+  __device__ void store(const Regs& g, unsigned char* tile) const {
+    S* lds = reinterpret_cast<S*>(tile);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (!act[i]) continue;
       S* base = lds + (cb[i] * TK) * KT<T>::LDK + kb[i] * TK;
       if constexpr (sizeof(S) == 2) {
-        // reg[i][q] = k-row q, columns 0..7 (dword d: columns 2d | 2d+1 << 16).
+        // g.v[i][q] = k-row q, columns 0..7 (dword d: columns 2d | 2d+1 << 16).
         // Column n, as 8 k values: dword e = k 2e | k 2e+1 << 16.
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           u32x4_t lo, hi;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t x = reg[i][2 * e][d], y = reg[i][2 * e + 1][d];
+            const uint32_t x = g.v[i][2 * e][d], y = g.v[i][2 * e + 1][d];
             lo[e] = (x & 0xffffu) | (y << 16);
             hi[e] = (x >> 16) | (y & 0xffff0000u);
           }
@@ -182,10 +237,10 @@ struct KColsLoader {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           u32x4_t col;
-          col[0] = reg[i][0][d];
-          col[1] = reg[i][1][d];
-          col[2] = reg[i][2][d];
-          col[3] = reg[i][3][d];
+          col[0] = g.v[i][0][d];
+          col[1] = g.v[i][1][d];
+          col[2] = g.v[i][2][d];
+          col[3] = g.v[i][3][d];
           *reinterpret_cast<u32x4_t*>(base + d * KT<T>::LDK) = col;
         }
       }
@@ -193,73 +248,129 @@ struct KColsLoader {
   }
 };
 
+template <class L> struct LayoutOf;
+template <class T, int R, int NW> struct LayoutOf<DmaRows<T, R, NW>> { typedef Swz<T> type; };
+template <class T, int R, int NT> struct LayoutOf<KColsLoader<T, R, NT>> { typedef Pad<T> type; };
+
+// Dynamic LDS of a kernel: two stages of (A tile, B tile), or the epilogue's
+// staging area (WTM x (BN + 4) fp32), whichever is larger.
+template <class C, class OA, class OB>
+struct Smem {
+  static constexpr size_t STAGE = OA::TILE_BYTES + OB::TILE_BYTES;
+  static constexpr size_t OPERANDS = 2 * STAGE;
+  static constexpr size_t EPI = (size_t)C::WTM * (C::BN + 4) * sizeof(float);
+  static constexpr size_t BYTES = OPERANDS > EPI ? OPERANDS : EPI;
+};
+
 // ---------------------------------------------------------------------------
-// One BK-deep step of the wave's tile from LDS.
+// One BK-deep step of the wave's tile from LDS.  Fragments are double
+// buffered across the k16 sub-steps: the LDS reads of sub-step s+1 are issued
+// before the MFMAs of sub-step s, so their latency hides behind 16 MFMAs.
 // ---------------------------------------------------------------------------
-template <class T, class C>
-__device__ __forceinline__ void mma_tile(const typename T::storage* As,
-                                         const typename T::storage* Bs, int wm, int wn,
-                                         int lane, f32x16_t (&acc)[C::FM][C::FN]) {
-  constexpr int BK = KT<T>::BK, LDK = KT<T>::LDK;
+template <class T, class C, class LA, class LB>
+__device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned char* Bb,
+                                         int wm, int wn, int lane,
+                                         f32x16_t (&acc)[C::FM][C::FN]) {
+  constexpr int STEPS = KT<T>::BK / T::kstep;
   const int r32 = lane & 31, hk = lane >> 5;
-#pragma unroll
-  for (int s = 0; s < BK / T::kstep; ++s) {
-    if constexpr (sizeof(typename T::storage) == 2) {
-      u32x4_t fa[C::FM], fb[C::FN];
+  if constexpr (sizeof(typename T::storage) == 2) {
+    u32x4_t fa[2][C::FM], fb[2][C::FN];
+    auto fetch = [&](int buf, int s) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
-        fa[i] = *reinterpret_cast<const u32x4_t*>(As + (wm * C::WTM + i * 32 + r32) * LDK +
-                                                   s * 16 + hk * 8);
+        fa[buf][i] = LA::frag16(Ab, wm * C::WTM + i * 32 + r32, 2 * s + hk);
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
-        fb[j] = *reinterpret_cast<const u32x4_t*>(Bs + (wn * C::WTN + j * 32 + r32) * LDK +
-                                                   s * 16 + hk * 8);
+        fb[buf][j] = LB::frag16(Bb, wn * C::WTN + j * 32 + r32, 2 * s + hk);
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      if (s + 1 < STEPS) fetch((s + 1) & 1, s + 1);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) T::mma(fa[i], fb[j], acc[i][j]);
-    } else {
-      float fa[C::FM], fb[C::FN];
+        for (int j = 0; j < C::FN; ++j) T::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+    }
+    // Keep that order through instruction scheduling: the first sub-step's
+    // reads, then each later sub-step's reads spread between the MFMAs of
+    // the sub-step before it (mask 0x100: LDS read, 0x008: MFMA).
+    constexpr int NR = C::FM + C::FN, NM = C::FM * C::FN;
+    static_assert(NM % NR == 0, "reads spread evenly over MFMAs");
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int s = 0; s + 1 < STEPS; ++s)
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+  } else {
+    float fa[2][C::FM], fb[2][C::FN];
+    auto fetch = [&](int buf, int s) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
-        fa[i] = As[(wm * C::WTM + i * 32 + r32) * LDK + s * 2 + hk];
+        fa[buf][i] = LA::frag4(Ab, wm * C::WTM + i * 32 + r32, 2 * s + hk);
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
-        fb[j] = Bs[(wn * C::WTN + j * 32 + r32) * LDK + s * 2 + hk];
+        fb[buf][j] = LB::frag4(Bb, wn * C::WTN + j * 32 + r32, 2 * s + hk);
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      if (s + 1 < STEPS) fetch((s + 1) & 1, s + 1);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) T::mma(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < C::FN; ++j) T::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
     }
   }
 }
 
-// The double-buffered k loop shared by the three kernels.
-template <class T, class C, class LA, class LB, class LoadA, class LoadB>
-__device__ __forceinline__ void main_loop(LA& la, LB& lb, LoadA load_a, LoadB load_b, int nk,
-                                          typename T::storage* As, typename T::storage* Bs,
-                                          int wm, int wn, int lane,
+// The k loop shared by the three kernels.  Two LDS stages.  In iteration t
+// the register-path loads of tile t+1 are issued first, then the direct
+// loads of tile t+1 into the other stage, then tile t is multiplied, then the
+// registers are transposed into the other stage; one wait + barrier ends the
+// iteration.  Register loads go first so that waiting for them never waits
+// for the direct loads issued after them.
+//   fa(regs, tile, k0): issue operand A's k-tile starting at k0 (direct loads
+//   write `tile`, register loads fill `regs`); fb likewise for B.
+template <class T, class C, class OA, class OB, class FA, class FB>
+__device__ __forceinline__ void main_loop(const OA& oa, const OB& ob, FA fa, FB fb, int nk,
+                                          unsigned char* smem, int wm, int wn, int lane,
                                           f32x16_t (&acc)[C::FM][C::FN]) {
+  typedef typename LayoutOf<OA>::type LA;
+  typedef typename LayoutOf<OB>::type LB;
   constexpr int BK = KT<T>::BK;
+  constexpr size_t ST = Smem<C, OA, OB>::STAGE;
   if (nk <= 0) return;
-  load_a(0);
-  load_b(0);
-  la.store(As);
-  lb.store(Bs);
-  __syncthreads();
+  typename OA::Regs ra;
+  typename OB::Regs rb;
+  auto A = [&](int st) { return smem + st * ST; };
+  auto B = [&](int st) { return smem + st * ST + OA::TILE_BYTES; };
+  if constexpr (!OA::kDirect) fa(ra, A(0), 0);
+  if constexpr (!OB::kDirect) fb(rb, B(0), 0);
+  if constexpr (OA::kDirect) fa(ra, A(0), 0);
+  if constexpr (OB::kDirect) fb(rb, B(0), 0);
+  if constexpr (!OA::kDirect) oa.store(ra, A(0));
+  if constexpr (!OB::kDirect) ob.store(rb, B(0));
+  wait_and_barrier<0>();
   for (int t = 0; t < nk; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < nk) {
-      load_a((t + 1) * BK);
-      load_b((t + 1) * BK);
+    const int cur = t & 1, nxt = cur ^ 1;
+    const bool more = t + 1 < nk;
+    if (more) {
+      if constexpr (!OA::kDirect) fa(ra, A(nxt), (t + 1) * BK);
+      if constexpr (!OB::kDirect) fb(rb, B(nxt), (t + 1) * BK);
+      if constexpr (OA::kDirect) fa(ra, A(nxt), (t + 1) * BK);
+      if constexpr (OB::kDirect) fb(rb, B(nxt), (t + 1) * BK);
     }
-    mma_tile<T, C>(As + cur * Lds<T, C>::A_ELEMS, Bs + cur * Lds<T, C>::B_ELEMS, wm, wn, lane,
-                   acc);
-    if (t + 1 < nk) {
-      la.store(As + (cur ^ 1) * Lds<T, C>::A_ELEMS);
-      lb.store(Bs + (cur ^ 1) * Lds<T, C>::B_ELEMS);
+    mma_tile<T, C, LA, LB>(A(cur), B(cur), wm, wn, lane, acc);
+    if (more) {
+      if constexpr (!OA::kDirect) oa.store(ra, A(nxt));
+      if constexpr (!OB::kDirect) ob.store(rb, B(nxt));
     }
-    __syncthreads();
+    wait_and_barrier<0>();
   }
 }
 
@@ -373,9 +484,9 @@ __device__ __forceinline__ float upstream_scale(const float* grad_output, float 
 template <class T, class C>
 __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   typedef typename T::storage S;
+  typedef DmaRows<T, C::BM, C::NT / 64> OA;
+  typedef DmaRows<T, C::BN, C::NT / 64> OB;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  S* As = reinterpret_cast<S*>(smem_raw);
-  S* Bs = As + 2 * Lds<T, C>::A_ELEMS;
   __shared__ int64_t tgt_s[C::BM];
 
   const int tiles_m = (a.rows + C::BM - 1) / C::BM;
@@ -399,8 +510,8 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint64_t)a.BT * a.H * sizeof(S));
   const int64_t nrows_w = a.V - n0 < C::BN ? a.V - n0 : C::BN;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + n0 * a.H, (uint64_t)nrows_w * a.H * sizeof(S));
-  KRowsLoader<T, C::BM, C::NT> la;
-  KRowsLoader<T, C::BN, C::NT> lb;
+  OA la;
+  OB lb;
   la.init(tid, [&](int r) -> uint32_t {
     const int gm = m0 + r;
     return gm < a.rows ? (uint32_t)a.idx[gm] * row_bytes : kOOB;
@@ -411,8 +522,9 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   zero_acc<C>(acc);
   const int K = (int)a.H;
   main_loop<T, C>(
-      la, lb, [&](int k0) { la.load(xr, k0, K); }, [&](int k0) { lb.load(wr, k0, K); },
-      (K + KT<T>::BK - 1) / KT<T>::BK, As, Bs, wm, wn, lane, acc);
+      la, lb, [&](auto&, unsigned char* tile, int k0) { la.dma(xr, tile, k0, K); },
+      [&](auto&, unsigned char* tile, int k0) { lb.dma(wr, tile, k0, K); },
+      (K + KT<T>::BK - 1) / KT<T>::BK, smem_raw, wm, wn, lane, acc);
 
   // Epilogue: store the logits, and per (row, 64-column block) the max and
   // the sum of exp(z - max) in fp32.  Both tile shapes reduce a 64-column
@@ -451,9 +563,9 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
 template <class T, class C>
 __global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
   typedef typename T::storage S;
+  typedef DmaRows<T, C::BM, C::NT / 64> OA;
+  typedef KColsLoader<T, C::BN, C::NT> OB;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  S* As = reinterpret_cast<S*>(smem_raw);
-  S* Bs = As + 2 * Lds<T, C>::A_ELEMS;
 
   const int tiles_m = (a.rows + C::BM - 1) / C::BM;
   const int tiles_n = (int)((a.H + C::BN - 1) / C::BN);
@@ -480,8 +592,8 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
   const __amdgpu_buffer_rsrc_t gr = make_rsrc(
       G + (int64_t)m0 * a.ldz + kbeg, ((uint64_t)g_rows * a.ldz - kbeg) * sizeof(S));
   const uint32_t w_row_bytes = (uint32_t)H * (uint32_t)sizeof(S);
-  KRowsLoader<T, C::BM, C::NT> la;
-  KColsLoader<T, C::BN, C::NT> lb;
+  OA la;
+  OB lb;
   la.init(tid, [&](int r) -> uint32_t { return r < g_rows ? (uint32_t)r * gz_bytes : kOOB; });
   lb.init(tid);
 
@@ -489,17 +601,17 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
   zero_acc<C>(acc);
   const int K = (int)(kend - kbeg);
   main_loop<T, C>(
-      la, lb, [&](int k0) { la.load(gr, k0, K); },
-      [&](int k0) {
+      la, lb, [&](auto&, unsigned char* tile, int k0) { la.dma(gr, tile, k0, K); },
+      [&](auto& g, unsigned char*, int k0) {
         // W rows of this k-tile: one descriptor per tile keeps offsets small.
         const int64_t r0 = kbeg + k0;
         const int64_t nr = kend_w - r0 < KT<T>::BK ? kend_w - r0 : KT<T>::BK;
         const __amdgpu_buffer_rsrc_t wr =
             make_rsrc(W + r0 * H, nr > 0 ? (uint64_t)nr * H * sizeof(S) : 0);
-        lb.load(wr, 0, [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * w_row_bytes : kOOB; },
-                n0, H);
+        lb.load(g, wr, 0,
+                [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * w_row_bytes : kOOB; }, n0, H);
       },
-      K > 0 ? (K + KT<T>::BK - 1) / KT<T>::BK : 0, As, Bs, wm, wn, lane, acc);
+      K > 0 ? (K + KT<T>::BK - 1) / KT<T>::BK : 0, smem_raw, wm, wn, lane, acc);
 
   const float sc = upstream_scale(a.grad_output, a.inv_n, a.reduction);
   S* dX = static_cast<S*>(a.dX);
@@ -555,9 +667,9 @@ __device__ __forceinline__ void rmw8(void* dW, int64_t o, float (&v)[8], bool ac
 template <class T, class C, class D>
 __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
   typedef typename T::storage S;
+  typedef KColsLoader<T, C::BM, C::NT> OA;
+  typedef DmaRows<T, C::BN, C::NT / 64> OB;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  S* As = reinterpret_cast<S*>(smem_raw);
-  S* Bs = As + 2 * Lds<T, C>::A_ELEMS;
 
   const int tiles_m = (int)((a.V + C::BM - 1) / C::BM);
   const int tiles_n = (int)((a.H + C::BN - 1) / C::BN);
@@ -578,8 +690,8 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
   const int xt_rows = H - n0 < C::BN ? H - n0 : C::BN;
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(XcT + (int64_t)n0 * a.ldx, (uint64_t)xt_rows * a.ldx * sizeof(S));
-  KColsLoader<T, C::BM, C::NT> la;
-  KRowsLoader<T, C::BN, C::NT> lb;
+  OA la;
+  OB lb;
   la.init(tid);
   lb.init(tid, [&](int r) -> uint32_t { return r < xt_rows ? (uint32_t)r * xt_row_bytes : kOOB; });
   const int ldz_cols = (int)a.ldz;
@@ -588,15 +700,16 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
   zero_acc<C>(acc);
   main_loop<T, C>(
       la, lb,
-      [&](int k0) {
+      [&](auto& g, unsigned char*, int k0) {
         const int nr = a.rows - k0 < KT<T>::BK ? a.rows - k0 : KT<T>::BK;
         const __amdgpu_buffer_rsrc_t gr =
             make_rsrc(G + (int64_t)k0 * a.ldz, nr > 0 ? (uint64_t)nr * a.ldz * sizeof(S) : 0);
-        la.load(gr, 0, [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * gz_bytes : kOOB; },
+        la.load(g, gr, 0,
+                [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * gz_bytes : kOOB; },
                 (int)m0, ldz_cols);
       },
-      [&](int k0) { lb.load(xr, k0, a.rows); }, (a.rows + KT<T>::BK - 1) / KT<T>::BK, As, Bs,
-      wm, wn, lane, acc);
+      [&](auto&, unsigned char* tile, int k0) { lb.dma(xr, tile, k0, a.rows); },
+      (a.rows + KT<T>::BK - 1) / KT<T>::BK, smem_raw, wm, wn, lane, acc);
 
   const float sc = upstream_scale(a.grad_output, a.inv_n, a.reduction);
   const bool accumulate = a.accumulate != 0;
@@ -623,27 +736,34 @@ static hipError_t allow_lds(K kernel, size_t bytes) {
 }
 
 template <class T, class C>
+struct LogitsSmem : Smem<C, DmaRows<T, C::BM, C::NT / 64>, DmaRows<T, C::BN, C::NT / 64>> {};
+template <class T, class C>
+struct DxSmem : Smem<C, DmaRows<T, C::BM, C::NT / 64>, KColsLoader<T, C::BN, C::NT>> {};
+template <class T, class C>
+struct DwSmem : Smem<C, KColsLoader<T, C::BM, C::NT>, DmaRows<T, C::BN, C::NT / 64>> {};
+
+template <class T, class C>
 static hipError_t launch_logits_t(const LogitsArgs& a, hipStream_t st) {
-  static const hipError_t prep = allow_lds(logits_kernel<T, C>, Lds<T, C>::BYTES);
+  static const hipError_t prep = allow_lds(logits_kernel<T, C>, LogitsSmem<T, C>::BYTES);
   if (prep != hipSuccess) return prep;
   const int tiles = ((a.rows + C::BM - 1) / C::BM) * (int)((a.V + C::BN - 1) / C::BN);
-  logits_kernel<T, C><<<dim3(tiles), dim3(C::NT), Lds<T, C>::BYTES, st>>>(a);
+  logits_kernel<T, C><<<dim3(tiles), dim3(C::NT), LogitsSmem<T, C>::BYTES, st>>>(a);
   return hipGetLastError();
 }
 template <class T, class C>
 static hipError_t launch_dx_t(const DxArgs& a, hipStream_t st) {
-  static const hipError_t prep = allow_lds(dx_kernel<T, C>, Lds<T, C>::BYTES);
+  static const hipError_t prep = allow_lds(dx_kernel<T, C>, DxSmem<T, C>::BYTES);
   if (prep != hipSuccess) return prep;
   const int tiles = ((a.rows + C::BM - 1) / C::BM) * (int)((a.H + C::BN - 1) / C::BN) * a.splits;
-  dx_kernel<T, C><<<dim3(tiles), dim3(C::NT), Lds<T, C>::BYTES, st>>>(a);
+  dx_kernel<T, C><<<dim3(tiles), dim3(C::NT), DxSmem<T, C>::BYTES, st>>>(a);
   return hipGetLastError();
 }
 template <class T, class C, class D>
 static hipError_t launch_dw_t(const DwArgs& a, hipStream_t st) {
-  static const hipError_t prep = allow_lds(dw_kernel<T, C, D>, Lds<T, C>::BYTES);
+  static const hipError_t prep = allow_lds(dw_kernel<T, C, D>, DwSmem<T, C>::BYTES);
   if (prep != hipSuccess) return prep;
   const int tiles = (int)((a.V + C::BM - 1) / C::BM) * (int)((a.H + C::BN - 1) / C::BN);
-  dw_kernel<T, C, D><<<dim3(tiles), dim3(C::NT), Lds<T, C>::BYTES, st>>>(a);
+  dw_kernel<T, C, D><<<dim3(tiles), dim3(C::NT), DwSmem<T, C>::BYTES, st>>>(a);
   return hipGetLastError();
 }
 
