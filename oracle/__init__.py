@@ -252,3 +252,28 @@ def flce_matmul(X, W, targets, *, ignore_index: int = -100, reduction: str = "me
     lse_full = np.full(BT, np.nan)
     lse_full[idx] = lse_l
     return dict(loss=loss, dX=dX, dW=dW, lse=lse_full, n_valid=N)
+
+
+def target_logits(Xd: np.ndarray, Wd: np.ndarray, targets, *, ignore_index: int = -100):
+    """z[i, t_i] = X_i . W_{t_i} for labelled rows (fp64; 0 for ignored rows)."""
+    t = _i64(targets)
+    lab = t != ignore_index
+    z = np.zeros(Xd.shape[0], dtype=np.float64)
+    rows = np.nonzero(lab)[0]
+    for s in range(0, rows.size, 4096):
+        r = rows[s:s + 4096]
+        z[r] = np.einsum("ij,ij->i", Xd[r], Wd[t[r]])
+    return z
+
+
+def loss_from_lse(lse: np.ndarray, zt: np.ndarray, targets, *, ignore_index: int = -100,
+                  reduction: str = "mean"):
+    """Cross-entropy from per-row lse and target logit: mean/sum scalar, or [BT] for none."""
+    t = _i64(targets)
+    lab = t != ignore_index
+    rows = np.where(lab, lse - zt, 0.0)
+    if reduction == "none":
+        return rows
+    tot = float(np.sum(rows[lab]))
+    n = int(lab.sum())
+    return (tot / n if n else 0.0) if reduction == "mean" else tot
