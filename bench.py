@@ -66,6 +66,15 @@ def parse():
                    help="comma-separated extra workloads reported under 'extra' ('' for none)")
     p.add_argument("--cpu-rows", type=int, default=16, help="rows in the oracle's timed sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run plain 1 GiB device copies (reference for HBM byte counters)")
+    p.add_argument("--record-traffic", nargs=4, metavar=("KERNEL", "WORKLOAD", "FETCH_CSV",
+                                                          "WRITE_CSV"),
+                   help="write profiles/KERNEL_WORKLOAD.traffic.txt from FETCH_SIZE and "
+                        "WRITE_SIZE collections that include --copy-calibration, and exit")
+    p.add_argument("--summarize-profile", nargs="+", metavar="CSV",
+                   help="print a text summary of rocprofv3 csv output (kernel stats, or "
+                        "FETCH_SIZE / WRITE_SIZE counter collections) and exit")
     return p.parse_args()
 
 
@@ -193,16 +202,138 @@ def cpu_baseline(host, cfg, rows):
                        f"{dt:.1f} s; widening the inputs to fp64 is not timed")
 
 
+# ---------------------------------------------------------------- profiling
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["linear_cross_entropy_chunked_amd/csrc/flce_gemm.hip",
+                  "linear_cross_entropy_chunked_amd/csrc/flce_rowops.hip",
+                  "linear_cross_entropy_chunked_amd/csrc/flce_device.hpp"]
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration(dev):
+    """Plain device copies of a known size: 1 GiB read + 1 GiB written per copy."""
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def summarize_profile(paths):
+    """Text summary of rocprofv3 csv files (kernel_stats or counter_collection)."""
+    import csv
+    import collections
+    for path in paths:
+        rows = list(csv.DictReader(open(path)))
+        print(f"## {os.path.basename(path)}")
+        if rows and "AverageNs" in rows[0]:
+            print(f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s} {'pct':>6s}")
+            for r in rows:
+                print(f"{r['Name'][:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.1f} "
+                      f"{float(r['TotalDurationNs'])/1e6:10.2f} {float(r['Percentage']):6.2f}")
+        else:
+            agg = collections.defaultdict(list)
+            for r in rows:
+                agg[(r["Kernel_Name"][:70], r["Counter_Name"])].append(float(r["Counter_Value"]))
+            print(f"{'kernel':70s} {'counter':12s} {'dispatches':>10s} {'avg_per_dispatch':>18s}")
+            for (k, c), v in sorted(agg.items()):
+                print(f"{k:70s} {c:12s} {len(v):10d} {sum(v)/len(v):18.1f}")
+        print()
+
+
+def _per_dispatch(path, match):
+    import csv
+    return [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if match(r["Kernel_Name"])]
+
+
+def record_traffic(kernel, workload, fetch_csv, write_csv):
+    """Calibrated HBM bytes per launch of one kernel kind, from counter collections.
+
+    FETCH_SIZE and WRITE_SIZE are in KiB per dispatch.  Each is scaled by
+    (bytes a 1 GiB plain copy really moves) / (what the counter reports for
+    that copy), taken from the --copy-calibration dispatches of the same run.
+    """
+    names = {"logits_gemm": "logits_kernel", "dx_gemm": "dx_kernel", "dw_gemm": "dw_kernel",
+             "softmax_grad": "softmax_kernel"}
+    kname = names[kernel]
+    copy_f = [v for v in _per_dispatch(fetch_csv, lambda n: "copyBuffer" in n) if v > 1e5]
+    copy_w = [v for v in _per_dispatch(write_csv, lambda n: "copyBuffer" in n) if v > 1e5]
+    ref_kib = COPY_BYTES / 1024
+    f_scale = ref_kib / (sum(copy_f) / len(copy_f))
+    w_scale = ref_kib / (sum(copy_w) / len(copy_w))
+    kf = _per_dispatch(fetch_csv, lambda n: kname in n)
+    kw = _per_dispatch(write_csv, lambda n: kname in n)
+    fetch = sum(kf) / len(kf) * 1024 * f_scale
+    write = sum(kw) / len(kw) * 1024 * w_scale
+    path = os.path.join(PROFILES, f"{kernel}_{workload}.traffic.txt")
+    with open(path, "w") as fh:
+        fh.write(f"# HBM traffic per launch of {kernel} ({kname}), workload {workload}\n")
+        fh.write("# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of:\n")
+        fh.write(f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- "
+                 f"python bench.py --workload {workload} --steps 1 --warmup 1 "
+                 f"--no-cpu-baseline --extra '' --copy-calibration\n")
+        fh.write("#   (the same with --pmc WRITE_SIZE -o write)\n")
+        fh.write("# counters are KiB per dispatch; each is scaled by the ratio of the bytes a\n")
+        fh.write("# 1 GiB device copy moves to what the counter reports for it\n")
+        fh.write(f"copy_fetch_kib_reported = {sum(copy_f) / len(copy_f):.1f}\n")
+        fh.write(f"copy_write_kib_reported = {sum(copy_w) / len(copy_w):.1f}\n")
+        fh.write(f"fetch_scale = {f_scale:.4f}\nwrite_scale = {w_scale:.4f}\n")
+        fh.write(f"dispatches = {len(kf)}\n")
+        fh.write(f"fetch_kib_per_dispatch = {sum(kf) / len(kf):.1f}\n")
+        fh.write(f"write_kib_per_dispatch = {sum(kw) / len(kw):.1f}\n")
+        fh.write(f"hbm_read_bytes_per_launch = {fetch:.6g}\n")
+        fh.write(f"hbm_write_bytes_per_launch = {write:.6g}\n")
+        fh.write(f"hbm_bytes_per_launch = {fetch + write:.6g}\n")
+        fh.write(f"kernel_source_sha = {kernel_source_hash()}\n")
+    print(open(path).read())
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch recorded from FETCH_SIZE / WRITE_SIZE counter runs, if current."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_hash():
+        return None  # the kernel changed since the counters were taken
+    return float(kv["hbm_bytes_per_launch"])
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {a.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if a.summarize_profile:
+        summarize_profile(a.summarize_profile)
+        return
+    if a.record_traffic:
+        record_traffic(*a.record_traffic)
+        return
     import torch
     import linear_cross_entropy_chunked_amd as pkg
     pkg.load()
     dev = torch.device("cuda:0")
+    if a.copy_calibration:
+        log("copy calibration: 2 x 1 GiB device copies")
+        copy_calibration(dev)
     cfg = WORKLOADS[a.workload]
     main_res, host = run_workload(a.workload, cfg, a.steps, a.warmup, dev)
     extras = {}
@@ -215,6 +346,7 @@ def main():
             hd = (host, (X.to(dev), W.to(dev), t.to(dev)))
         extras[name], _ = run_workload(name, ecfg, max(a.steps // 2, 2), a.warmup, dev, hd)
     rl = roofline(main_res, cfg)
+    rl["traffic"] = recorded_traffic(rl["kernel"], a.workload)
     out = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],

@@ -380,3 +380,18 @@ def test_planted_mistake_is_caught(oracle_mod, tmp_path, name, old, new):
     finally:
         oracle_mod._lib = saved
     assert _pins_pass(oracle_mod)
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_loss_from_lse_and_target_logits_match_full_oracle(oracle_mod, reduction):
+    """The helpers the full-size GPU tests use reproduce the loop oracle's loss."""
+    X, W, t = _case(BT=41, H=7, V=19, seed=27, frac=0.3)
+    full = oracle_mod.flce(X, W, t, reduction=reduction)
+    Xd, Wd = oracle_mod.widen(X), oracle_mod.widen(W)
+    lse = oracle_mod.lse_matmul(Xd, Wd, t)
+    zt = oracle_mod.target_logits(Xd, Wd, t)
+    got = oracle_mod.loss_from_lse(lse, zt, t, reduction=reduction)
+    np.testing.assert_allclose(got, full["loss"], rtol=1e-13, atol=1e-15)
+    # and against torch's cross_entropy (library routine)
+    l_ref, _, _ = _torch_ref(Xd, Wd, t.numpy(), reduction, None)
+    np.testing.assert_allclose(got, l_ref, rtol=1e-12, atol=1e-14)
