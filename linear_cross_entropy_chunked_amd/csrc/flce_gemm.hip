@@ -4,22 +4,21 @@
 //
 //   logits  Z[m, n]  = sum_k X[idx[m], k] * W[n, k]        (A k-contiguous, B k-contiguous)
 //   dX      dX[idx[m], n] = s * sum_k G[m, k] * W[k, n]    (A k-contiguous, B n-contiguous)
-//   dW      dW[m, n] (+)= s * sum_k G[k, m] * X[idx[k], n] (A m-contiguous, B n-contiguous)
+//   dW      dW[m, n] (+)= s * sum_k G[k, m] * Xc[k, n]     (A m-contiguous, B k-contiguous)
 //
-// One main loop serves all three.  Both operands are staged through LDS in a
-// k-contiguous layout (rows padded by 16 bytes), so each lane reads an MFMA
-// fragment with one 16-byte LDS read and 8 consecutive lanes hit 8 distinct
-// bank groups.  Operands that are contiguous along M or N in memory are
-// transposed in registers in 8x8 (16-bit) or 4x4 (fp32) blocks; lanes are
-// laid out k-block fastest so that both the global loads (128 contiguous
-// bytes per row) and the 16-byte LDS writes are conflict-free.  Two LDS
-// buffers: the next k-tile's global loads are in flight while the current
-// one is multiplied.
+// One main loop serves all three.  Every operand tile goes from global memory
+// straight into LDS (buffer_load ... lds, 16 bytes per lane), in the layout it
+// has in memory: k-contiguous tiles as rows of k, m/n-contiguous tiles as
+// rows of m/n, both with an XOR swizzle of their 16-byte chunks.  MFMA
+// fragments are read with 16-byte LDS reads (k-contiguous tiles) or with two
+// transposing 8-byte reads (m/n-contiguous tiles); the swizzles keep both
+// kinds free of bank conflicts on gfx950's 64-bank LDS.  Two LDS stages: the
+// next k-tile streams in while the current one is multiplied.
 //
 // Two tile shapes: 256x256 blocks of four 128x128 waves (one workgroup per
-// CU, 144 KiB of LDS) for the compute-bound shapes, and 128x128 blocks of four
-// 64x64 waves (two workgroups per CU) where the problem is small or, for
-// grad_weight with few rows per chunk, bound by the read-modify-write of dW.
+// CU) for the compute-bound shapes, and 128x128 blocks of four 64x64 waves
+// (two workgroups per CU) where the problem is small or, for grad_weight with
+// few rows per chunk, bound by the read-modify-write of dW.
 #include <type_traits>
 
 #include "flce_device.hpp"
@@ -38,12 +37,20 @@ struct Cfg {
 typedef Cfg<256, 256> Big;
 typedef Cfg<128, 128> Small;
 
+// k-tile geometry: every LDS row of a k-contiguous tile holds kKBytes bytes
+// of k (BK = 64 bf16/fp16, 32 fp32), and tiles rotate through kStages LDS
+// buffers so that each one's loads have kStages - 1 k-tiles of MFMA work to
+// arrive in.  (Measured on MI355X: 128-byte rows with two stages beat
+// 64-byte rows with two to four stages.)
+constexpr int kKBytes = 128;
+constexpr int kStages = 2;
+
 template <class T>
-struct KT {  // k-tile geometry per element type
+struct KT {
   typedef typename T::storage S;
-  static constexpr int BK = (sizeof(S) == 2) ? 64 : 32;  // 128 bytes of k per row
-  static constexpr int LDK = BK + 16 / (int)sizeof(S);  // padded row of the register path
-  static constexpr int RB = BK * (int)sizeof(S);          // bytes per row, swizzled layout
+  static constexpr int BK = kKBytes / (int)sizeof(S);
+  static constexpr int RB = kKBytes;
+  static constexpr int STEPS = BK / T::kstep;  // MFMA k-steps per k-tile
 };
 
 // ---------------------------------------------------------------------------
@@ -59,9 +66,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,
                                            0x00020000);
 }
-__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-}
 // 16 bytes per lane straight into LDS: lane i of the wave writes lds + 16 i.
 __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                                unsigned char* lds) {
@@ -69,10 +73,10 @@ __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_
       r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
 }
 
-// Wait until at most `vm` vector-memory loads of this wave are outstanding
+// Wait until at most `VM` vector-memory loads of this wave are outstanding
 // and all its LDS operations are done, then meet the other waves.  A plain
 // s_barrier: the workgroup fence of __syncthreads would also wait for the
-// loads still streaming into the other LDS buffer.
+// loads still streaming into the other LDS buffers.
 template <int VM>
 __device__ __forceinline__ void wait_and_barrier() {
   static_assert(VM >= 0 && VM < 64, "vmcnt range");
@@ -84,204 +88,227 @@ __device__ __forceinline__ void wait_and_barrier() {
 }
 
 // ---------------------------------------------------------------------------
-// LDS layouts of an R x BK operand tile (k contiguous within a row).
-//   Swz: rows of RB = 128 bytes, unpadded, 16-byte chunks XOR-swizzled by
-//        row: physical chunk p of row r holds k-chunk p ^ (r % 8).  Filled
-//        directly from global memory; 8 lanes reading one chunk of 8
-//        consecutive rows hit 8 distinct bank groups.
-//   Pad: rows of LDK elements (16-byte pad), filled from registers.
-// frag16: the 16 bytes of k-chunk kc of row r; frag4: element k of row r.
+// LDS layouts of an operand tile, both filled straight from global memory in
+// 16-byte chunks and both read as MFMA fragments without bank conflicts.
+//
+// RowSwz: R rows x BK (k contiguous), rows of RB bytes, unpadded; the 16-byte
+//   chunk index is XORed with a function of the row so that the 16 lanes
+//   reading one k-chunk of 16 consecutive rows hit 16 distinct 16-byte slots.
+// ColSwz: BK k-rows x R (m or n contiguous, as in memory), rows of R * s
+//   bytes, chunk index XORed with a function of k.  A 16-bit
+//   fragment (8 consecutive k of one column per lane) is gathered with two
+//   transposing reads (ds_read_b64_tr_b16): within each group of 16 lanes,
+//   lane q points at 4 elements of row k0 + q / 4, columns c0 + 4 (q % 4), and
+//   lane l then receives rows k0..k0+3 of column c0 + l.  The XOR puts the 4
+//   rows' 64-byte pieces (two lane groups) in distinct bank groups.  fp32
+//   fragments are single elements and need no transpose.
+// frag16(b, c, s, lane): the 16-bit fragment of tile row/column c for k-step
+//   s; frag4(b, c, k): the fp32 element (c, k).
 // ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(4))) short v4i16_t;
+
 template <class T>
-struct Swz {
+struct RowSwz {
   typedef typename T::storage S;
   static constexpr int RB = KT<T>::RB;
-  static_assert(RB == 128, "swizzle assumes 128-byte rows");
+  static_assert(RB == 64 || RB == 128, "row swizzle assumes 64- or 128-byte rows");
   static constexpr size_t bytes(int R) { return (size_t)R * RB; }
-  __device__ static const unsigned char* chunk(const unsigned char* b, int r, int kc) {
-    return b + r * RB + ((kc ^ (r & 7)) << 4);
-  }
-  __device__ static u32x4_t frag16(const unsigned char* b, int r, int kc) {
-    return *reinterpret_cast<const u32x4_t*>(chunk(b, r, kc));
+  // LDS serves 256 bytes per cycle (64 banks): the 16 rows read by 16
+  // consecutive lanes must land in 16 distinct 16-byte slots of that window.
+  // 128-byte rows: chunk ^= (r / 2) % 8; 64-byte rows: chunk ^= (r / 4) % 4.
+  __device__ static int swz(int r) { return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+  __device__ static u32x4_t frag16(const unsigned char* b, int r, int s, int lane) {
+    const int kc = 2 * s + (lane >> 5);
+    return *reinterpret_cast<const u32x4_t*>(b + r * RB + ((kc ^ swz(r)) << 4));
   }
   __device__ static float frag4(const unsigned char* b, int r, int k) {
-    return reinterpret_cast<const float*>(chunk(b, r, k >> 2))[k & 3];
+    return reinterpret_cast<const float*>(b + r * RB + (((k >> 2) ^ swz(r)) << 4))[k & 3];
   }
 };
-template <class T>
-struct Pad {
+
+template <class T, int R>
+struct ColSwz {
   typedef typename T::storage S;
-  static constexpr int LDK = KT<T>::LDK;
-  static constexpr size_t bytes(int R) { return (size_t)R * LDK * sizeof(S); }
-  __device__ static u32x4_t frag16(const unsigned char* b, int r, int kc) {
-    return *reinterpret_cast<const u32x4_t*>(b + (r * LDK) * sizeof(S) + kc * 16);
+  static constexpr int RBT = R * (int)sizeof(S);  // bytes per k-row
+  static constexpr int EPC = 16 / (int)sizeof(S); // elements per 16-byte chunk
+  static constexpr size_t bytes(int) { return (size_t)KT<T>::BK * RBT; }
+  // 16-bit: the 4 k-rows of one transposing read move by 64 bytes each
+  // (chunk ^= 4 (k % 4)); fp32: odd k-rows move by 128 bytes (chunk ^= 8 (k % 2)).
+  static_assert(RBT >= 256, "column swizzle needs 16 chunks per k-row");
+  __device__ static int swz(int k) { return sizeof(S) == 2 ? 4 * (k & 3) : 8 * (k & 1); }
+  __device__ static const unsigned char* at(const unsigned char* b, int k, int c) {
+    return b + k * RBT + (((c / EPC) ^ swz(k)) << 4) + (c % EPC) * (int)sizeof(S);
   }
-  __device__ static float frag4(const unsigned char* b, int r, int k) {
-    return reinterpret_cast<const float*>(b)[r * LDK + k];
+  // c: first column of the 32-column MFMA block
+  __device__ static u32x4_t frag16(const unsigned char* b, int c, int s, int lane) {
+    const int q = lane & 15;
+    const int col = c + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
+    const int k1 = 16 * s + 8 * (lane >> 5) + (q >> 2);
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16_t*)at(b, k1, col));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16_t*)at(b, k1 + 4, col));
+    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+    return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+  }
+  __device__ static float frag4(const unsigned char* b, int c, int k) {
+    return *reinterpret_cast<const float*>(at(b, k, c));
   }
 };
 
 // ---------------------------------------------------------------------------
-// Operand tile loaders.
+// Operand tile loaders: each wave instruction moves 1 KiB (64 lanes x 16
+// bytes) from global memory into consecutive LDS bytes.
 // ---------------------------------------------------------------------------
 
-// k-contiguous source, straight into a Swz tile.  Tile row r starts at byte
-// offset rowoff(r) (kOOB: zero row) of the descriptor.  Each wave instruction
-// fills 8 rows (1 KiB): lane L takes row L / 8 of the group and physical chunk
-// L % 8, i.e. k-chunk (L % 8) ^ (L / 8).  Chunks whose first k is >= kend read
-// as zero; callers keep kend a multiple of the chunk width, and elements
-// between the logical K and kend are zero in memory.
+// k-contiguous source into a RowSwz tile.  Tile row r starts at byte offset
+// rowoff(r) (kOOB: zero row) of the descriptor.  An instruction fills RPI =
+// 1024 / RB rows: lane L takes row L / CPR of its group and physical chunk
+// L % CPR, i.e. k-chunk (L % CPR) ^ swz(row).  Chunks whose first k is >= kend read as zero;
+// callers keep kend a multiple of the chunk width, and elements between the
+// logical K and kend are zero in memory.
 template <class T, int R, int NWAVES>
 struct DmaRows {
-  static constexpr bool kDirect = true;
+  typedef RowSwz<T> Layout;
   typedef typename T::storage S;
-  static constexpr int RPI = 1024 / KT<T>::RB;  // rows per instruction
-  static constexpr int NI = R / RPI / NWAVES;    // instructions per wave per k-tile
+  static constexpr int CPR = KT<T>::RB / 16;
+  static constexpr int RPI = 1024 / KT<T>::RB;
+  static constexpr int NI = R / RPI / NWAVES;  // instructions per wave per k-tile
   static_assert(R % (RPI * NWAVES) == 0, "tile rows not divisible among waves");
-  static constexpr size_t TILE_BYTES = Swz<T>::bytes(R);
-  struct Regs {};
+  static constexpr size_t TILE_BYTES = Layout::bytes(R);
   uint32_t roff[NI];
-  int kc_el;  // first k (elements) of this lane's chunk
+  int kc_el[NI];  // first k (elements) of this lane's chunk in each instruction
   int wave;
 
   template <class RowFn>
   __device__ void init(int tid, RowFn rowoff) {
     const int lane = tid & 63;
     wave = tid >> 6;
-    const int rin = lane / 8;
-    kc_el = ((lane & 7) ^ rin) * T::vec;
+    const int rin = lane / CPR;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) roff[i] = rowoff((wave + i * NWAVES) * RPI + rin);
+    for (int i = 0; i < NI; ++i) {
+      const int row = (wave + i * NWAVES) * RPI + rin;
+      roff[i] = rowoff(row);
+      kc_el[i] = ((lane % CPR) ^ Layout::swz(row)) * T::vec;
+    }
   }
-  __device__ void dma(__amdgpu_buffer_rsrc_t rs, unsigned char* tile, int k0, int kend) const {
-    const int k = k0 + kc_el;
-    const bool kin = k < kend;
-    const uint32_t kb = (uint32_t)k * (uint32_t)sizeof(S);
+  __device__ void issue(__amdgpu_buffer_rsrc_t rs, unsigned char* tile, int k0, int kend) const {
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      buf_load16_lds(rs, (kin && roff[i] != kOOB) ? roff[i] + kb : kOOB,
+    for (int i = 0; i < NI; ++i) {
+      const int k = k0 + kc_el[i];
+      buf_load16_lds(rs,
+                     (k < kend && roff[i] != kOOB) ? roff[i] + (uint32_t)k * (uint32_t)sizeof(S)
+                                                   : kOOB,
                      tile + (wave + i * NWAVES) * 1024);
+    }
   }
 };
 
-// Source contiguous along the tile's row index, into a Pad tile: tile element
-// (r, k) sits at byte offset rowoff(k) + (c0 + r) * sizeof(S) of the
+// Source contiguous along the tile's columns into a ColSwz tile: tile element
+// (k, c) sits at byte offset rowoff(k) + (c0 + c) * sizeof(S) of the
 // descriptor, rowoff(k) == kOOB for a zero k-row; columns at or past cend
-// read as zero (vector granularity).  Each thread moves a TK x TK block (TK =
-// elements per 16 bytes: 8 k-rows x 8 columns for 16-bit types, 4 x 4 for
-// fp32) and transposes it in registers.  Lane order is k-block fastest, so a
-// wave's global reads cover 128 contiguous bytes per row and its 16-byte LDS
-// writes fall in distinct banks.
-template <class T, int R, int NT>
-struct KColsLoader {
-  static constexpr bool kDirect = false;
+// read as zero (chunk granularity).  An instruction fills RPI = 1024 / (R *
+// s) k-rows; lane L takes k-row L / CPRT of its group and physical chunk
+// L % CPRT.
+template <class T, int R, int NWAVES>
+struct DmaCols {
+  typedef ColSwz<T, R> Layout;
   typedef typename T::storage S;
-  static constexpr int TK = T::vec;
-  static constexpr int BK = KT<T>::BK;
-  static constexpr int KBN = BK / TK;             // k blocks per tile
-  static constexpr int NBLK = (R / TK) * KBN;     // blocks per tile
-  static constexpr int NB = (NBLK + NT - 1) / NT; // blocks per thread
-  static constexpr size_t TILE_BYTES = Pad<T>::bytes(R);
-  struct Regs {
-    u32x4_t v[NB][TK];
-  };
-  int cb[NB], kb[NB];
-  bool act[NB];
+  static constexpr int RBT = Layout::RBT;
+  static_assert(RBT <= 1024 && 1024 % RBT == 0, "k-row must divide 1 KiB");
+  static constexpr int CPRT = RBT / 16;
+  static constexpr int RPI = 1024 / RBT;
+  static constexpr int NI = KT<T>::BK / RPI / NWAVES;
+  static_assert(KT<T>::BK % (RPI * NWAVES) == 0, "k-rows not divisible among waves");
+  static constexpr size_t TILE_BYTES = Layout::bytes(R);
+  int krow[NI];      // k-row within the tile of each instruction
+  uint32_t cofs[NI]; // byte offset of this lane's column chunk (kOOB: outside)
+  int wave;
 
-  __device__ void init(int tid) {
+  __device__ void init(int tid, int c0, int cend) {
+    const int lane = tid & 63;
+    wave = tid >> 6;
+    const int rin = lane / CPRT, p = lane % CPRT;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int b = tid + i * NT;
-      act[i] = b < NBLK;
-      kb[i] = b % KBN;
-      cb[i] = b / KBN;
+    for (int i = 0; i < NI; ++i) {
+      krow[i] = (wave + i * NWAVES) * RPI + rin;
+      const int c = c0 + (p ^ Layout::swz(krow[i])) * Layout::EPC;
+      cofs[i] = c < cend ? (uint32_t)c * (uint32_t)sizeof(S) : kOOB;
     }
   }
   template <class KFn>
-  __device__ void load(Regs& g, __amdgpu_buffer_rsrc_t rs, int k0, KFn rowoff, int c0,
-                       int cend) const {
+  __device__ void issue(__amdgpu_buffer_rsrc_t rs, unsigned char* tile, int k0,
+                        KFn rowoff) const {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int c = c0 + cb[i] * TK;
-      const bool col_ok = act[i] && c < cend;
-      const uint32_t cofs = (uint32_t)c * (uint32_t)sizeof(S);
-#pragma unroll
-      for (int q = 0; q < TK; ++q) {
-        const uint32_t ro = rowoff(k0 + kb[i] * TK + q);
-        g.v[i][q] = buf_load16(rs, (col_ok && ro != kOOB) ? ro + cofs : kOOB);
-      }
-    }
-  }
-  __device__ void store(const Regs& g, unsigned char* tile) const {
-    S* lds = reinterpret_cast<S*>(tile);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (!act[i]) continue;
-      S* base = lds + (cb[i] * TK) * KT<T>::LDK + kb[i] * TK;
-      if constexpr (sizeof(S) == 2) {
-        // g.v[i][q] = k-row q, columns 0..7 (dword d: columns 2d | 2d+1 << 16).
-        // Column n, as 8 k values: dword e = k 2e | k 2e+1 << 16.
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          u32x4_t lo, hi;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t x = g.v[i][2 * e][d], y = g.v[i][2 * e + 1][d];
-            lo[e] = (x & 0xffffu) | (y << 16);
-            hi[e] = (x >> 16) | (y & 0xffff0000u);
-          }
-          *reinterpret_cast<u32x4_t*>(base + (2 * d) * KT<T>::LDK) = lo;
-          *reinterpret_cast<u32x4_t*>(base + (2 * d + 1) * KT<T>::LDK) = hi;
-        }
-      } else {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          u32x4_t col;
-          col[0] = g.v[i][0][d];
-          col[1] = g.v[i][1][d];
-          col[2] = g.v[i][2][d];
-          col[3] = g.v[i][3][d];
-          *reinterpret_cast<u32x4_t*>(base + d * KT<T>::LDK) = col;
-        }
-      }
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t ro = rowoff(k0 + krow[i]);
+      buf_load16_lds(rs, (ro != kOOB && cofs[i] != kOOB) ? ro + cofs[i] : kOOB,
+                     tile + (wave + i * NWAVES) * 1024);
     }
   }
 };
 
-template <class L> struct LayoutOf;
-template <class T, int R, int NW> struct LayoutOf<DmaRows<T, R, NW>> { typedef Swz<T> type; };
-template <class T, int R, int NT> struct LayoutOf<KColsLoader<T, R, NT>> { typedef Pad<T> type; };
-
-// Dynamic LDS of a kernel: two stages of (A tile, B tile), or the epilogue's
-// staging area (WTM x (BN + 4) fp32), whichever is larger.
+// Dynamic LDS of a kernel: kStages stages of (A tile, B tile), or the
+// epilogue's staging area (WTM x (BN + 4) fp32), whichever is larger.
 template <class C, class OA, class OB>
 struct Smem {
   static constexpr size_t STAGE = OA::TILE_BYTES + OB::TILE_BYTES;
-  static constexpr size_t OPERANDS = 2 * STAGE;
+  static constexpr size_t OPERANDS = kStages * STAGE;
   static constexpr size_t EPI = (size_t)C::WTM * (C::BN + 4) * sizeof(float);
   static constexpr size_t BYTES = OPERANDS > EPI ? OPERANDS : EPI;
+  static constexpr int VMEM_PER_TILE = OA::NI + OB::NI;
 };
 
+// Fragment address helpers: a RowSwz operand is addressed by its row, a
+// ColSwz operand by the first column of the 32-wide MFMA block.
+template <class L> struct IsCol { static constexpr bool value = false; };
+template <class T, int R> struct IsCol<ColSwz<T, R>> { static constexpr bool value = true; };
+
+template <class L>
+__device__ __forceinline__ u32x4_t frag16_of(const unsigned char* b, int blk, int s, int lane) {
+  if constexpr (IsCol<L>::value)
+    return L::frag16(b, blk, s, lane);
+  else
+    return L::frag16(b, blk + (lane & 31), s, lane);
+}
+template <class L>
+__device__ __forceinline__ float frag4_of(const unsigned char* b, int blk, int s, int lane) {
+  return L::frag4(b, blk + (lane & 31), 2 * s + (lane >> 5));
+}
+
 // ---------------------------------------------------------------------------
-// One BK-deep step of the wave's tile from LDS.  Fragments are double
-// buffered across the k16 sub-steps: the LDS reads of sub-step s+1 are issued
-// before the MFMAs of sub-step s, so their latency hides behind 16 MFMAs.
+// One k-tile of the wave's tile from LDS.  Fragments are double buffered
+// across the MFMA k-steps: the LDS reads of step s+1 are issued before the
+// MFMAs of step s, and the interleave is pinned for the scheduler.
 // ---------------------------------------------------------------------------
+// Scheduling groups: NR LDS reads (mask 0x100) spread evenly between NM
+// MFMAs (mask 0x008), read q followed by its share of MFMAs.
+template <int NR, int NM, int Q = 0>
+struct PinInterleave {
+  __device__ static void run() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    constexpr int m = (NM * (Q + 1)) / NR - (NM * Q) / NR;
+    if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+    PinInterleave<NR, NM, Q + 1>::run();
+  }
+};
+template <int NR, int NM>
+struct PinInterleave<NR, NM, NR> {
+  __device__ static void run() {}
+};
+
 template <class T, class C, class LA, class LB>
 __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned char* Bb,
                                          int wm, int wn, int lane,
                                          f32x16_t (&acc)[C::FM][C::FN]) {
-  constexpr int STEPS = KT<T>::BK / T::kstep;
-  const int r32 = lane & 31, hk = lane >> 5;
+  constexpr int STEPS = KT<T>::STEPS;
   if constexpr (sizeof(typename T::storage) == 2) {
     u32x4_t fa[2][C::FM], fb[2][C::FN];
     auto fetch = [&](int buf, int s) {
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-        fa[buf][i] = LA::frag16(Ab, wm * C::WTM + i * 32 + r32, 2 * s + hk);
+      for (int i = 0; i < C::FM; ++i) fa[buf][i] = frag16_of<LA>(Ab, wm * C::WTM + i * 32, s, lane);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        fb[buf][j] = LB::frag16(Bb, wn * C::WTN + j * 32 + r32, 2 * s + hk);
+      for (int j = 0; j < C::FN; ++j) fb[buf][j] = frag16_of<LB>(Bb, wn * C::WTN + j * 32, s, lane);
     };
     fetch(0, 0);
 #pragma unroll
@@ -292,29 +319,20 @@ __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) T::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
     }
-    // Keep that order through instruction scheduling: the first sub-step's
-    // reads, then each later sub-step's reads spread between the MFMAs of
-    // the sub-step before it (mask 0x100: LDS read, 0x008: MFMA).
-    constexpr int NR = C::FM + C::FN, NM = C::FM * C::FN;
-    static_assert(NM % NR == 0, "reads spread evenly over MFMAs");
+    // reads per step: one per RowSwz fragment, two per ColSwz fragment
+    constexpr int NR = C::FM * (IsCol<LA>::value ? 2 : 1) + C::FN * (IsCol<LB>::value ? 2 : 1);
+    constexpr int NM = C::FM * C::FN;
     __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
-    for (int s = 0; s + 1 < STEPS; ++s)
-#pragma unroll
-      for (int q = 0; q < NR; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, NM / NR, 0);
-      }
+    for (int s = 0; s + 1 < STEPS; ++s) PinInterleave<NR, NM>::run();
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   } else {
     float fa[2][C::FM], fb[2][C::FN];
     auto fetch = [&](int buf, int s) {
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-        fa[buf][i] = LA::frag4(Ab, wm * C::WTM + i * 32 + r32, 2 * s + hk);
+      for (int i = 0; i < C::FM; ++i) fa[buf][i] = frag4_of<LA>(Ab, wm * C::WTM + i * 32, s, lane);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        fb[buf][j] = LB::frag4(Bb, wn * C::WTN + j * 32 + r32, 2 * s + hk);
+      for (int j = 0; j < C::FN; ++j) fb[buf][j] = frag4_of<LB>(Bb, wn * C::WTN + j * 32, s, lane);
     };
     fetch(0, 0);
 #pragma unroll
@@ -328,50 +346,42 @@ __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned
   }
 }
 
-// The k loop shared by the three kernels.  Two LDS stages.  In iteration t
-// the register-path loads of tile t+1 are issued first, then the direct
-// loads of tile t+1 into the other stage, then tile t is multiplied, then the
-// registers are transposed into the other stage; one wait + barrier ends the
-// iteration.  Register loads go first so that waiting for them never waits
-// for the direct loads issued after them.
-//   fa(regs, tile, k0): issue operand A's k-tile starting at k0 (direct loads
-//   write `tile`, register loads fill `regs`); fb likewise for B.
-template <class T, class C, class OA, class OB, class FA, class FB>
-__device__ __forceinline__ void main_loop(const OA& oa, const OB& ob, FA fa, FB fb, int nk,
-                                          unsigned char* smem, int wm, int wn, int lane,
-                                          f32x16_t (&acc)[C::FM][C::FN]) {
-  typedef typename LayoutOf<OA>::type LA;
-  typedef typename LayoutOf<OB>::type LB;
+// The k loop shared by the three kernels: kStages LDS stages.  Before tile t
+// is multiplied, each wave waits until its own loads of tile t are done
+// (loads of the next kStages - 2 tiles may still be in flight) and meets the
+// other waves; then the loads of tile t + kStages - 1 go into the stage that
+// tile t - 1 used, which every wave has finished reading.
+//   ia(tile, k0) / ib(tile, k0): issue operand A's / B's k-tile at k0 into `tile`.
+template <class T, class C, class OA, class OB, class IA, class IB>
+__device__ __forceinline__ void main_loop(IA ia, IB ib, int nk, unsigned char* smem, int wm, int wn,
+                                          int lane, f32x16_t (&acc)[C::FM][C::FN]) {
+  typedef typename OA::Layout LA;
+  typedef typename OB::Layout LB;
   constexpr int BK = KT<T>::BK;
   constexpr size_t ST = Smem<C, OA, OB>::STAGE;
+  constexpr int VM = (kStages - 2) * Smem<C, OA, OB>::VMEM_PER_TILE;
   if (nk <= 0) return;
-  typename OA::Regs ra;
-  typename OB::Regs rb;
-  auto A = [&](int st) { return smem + st * ST; };
-  auto B = [&](int st) { return smem + st * ST + OA::TILE_BYTES; };
-  if constexpr (!OA::kDirect) fa(ra, A(0), 0);
-  if constexpr (!OB::kDirect) fb(rb, B(0), 0);
-  if constexpr (OA::kDirect) fa(ra, A(0), 0);
-  if constexpr (OB::kDirect) fb(rb, B(0), 0);
-  if constexpr (!OA::kDirect) oa.store(ra, A(0));
-  if constexpr (!OB::kDirect) ob.store(rb, B(0));
-  wait_and_barrier<0>();
+#pragma unroll
+  for (int j = 0; j < kStages - 1; ++j)
+    if (j < nk) {
+      ia(smem + j * ST, j * BK);
+      ib(smem + j * ST + OA::TILE_BYTES, j * BK);
+    }
   for (int t = 0; t < nk; ++t) {
-    const int cur = t & 1, nxt = cur ^ 1;
-    const bool more = t + 1 < nk;
-    if (more) {
-      if constexpr (!OA::kDirect) fa(ra, A(nxt), (t + 1) * BK);
-      if constexpr (!OB::kDirect) fb(rb, B(nxt), (t + 1) * BK);
-      if constexpr (OA::kDirect) fa(ra, A(nxt), (t + 1) * BK);
-      if constexpr (OB::kDirect) fb(rb, B(nxt), (t + 1) * BK);
+    if (t + kStages - 2 < nk)
+      wait_and_barrier<VM>();
+    else
+      wait_and_barrier<0>();
+    const int tn = t + kStages - 1;
+    if (tn < nk) {
+      unsigned char* st = smem + (tn % kStages) * ST;
+      ia(st, tn * BK);
+      ib(st + OA::TILE_BYTES, tn * BK);
     }
-    mma_tile<T, C, LA, LB>(A(cur), B(cur), wm, wn, lane, acc);
-    if (more) {
-      if constexpr (!OA::kDirect) oa.store(ra, A(nxt));
-      if constexpr (!OB::kDirect) ob.store(rb, B(nxt));
-    }
-    wait_and_barrier<0>();
+    const unsigned char* cur = smem + (t % kStages) * ST;
+    mma_tile<T, C, LA, LB>(cur, cur + OA::TILE_BYTES, wm, wn, lane, acc);
   }
+  wait_and_barrier<0>();
 }
 
 template <class C>
@@ -521,9 +531,9 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
   const int K = (int)a.H;
-  main_loop<T, C>(
-      la, lb, [&](auto&, unsigned char* tile, int k0) { la.dma(xr, tile, k0, K); },
-      [&](auto&, unsigned char* tile, int k0) { lb.dma(wr, tile, k0, K); },
+  main_loop<T, C, OA, OB>(
+      [&](unsigned char* tile, int k0) { la.issue(xr, tile, k0, K); },
+      [&](unsigned char* tile, int k0) { lb.issue(wr, tile, k0, K); },
       (K + KT<T>::BK - 1) / KT<T>::BK, smem_raw, wm, wn, lane, acc);
 
   // Epilogue: store the logits, and per (row, 64-column block) the max and
@@ -564,7 +574,7 @@ template <class T, class C>
 __global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
   typedef typename T::storage S;
   typedef DmaRows<T, C::BM, C::NT / 64> OA;
-  typedef KColsLoader<T, C::BN, C::NT> OB;
+  typedef DmaCols<T, C::BN, C::NT / 64> OB;
   extern __shared__ __align__(16) unsigned char smem_raw[];
 
   const int tiles_m = (a.rows + C::BM - 1) / C::BM;
@@ -595,21 +605,21 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
   OA la;
   OB lb;
   la.init(tid, [&](int r) -> uint32_t { return r < g_rows ? (uint32_t)r * gz_bytes : kOOB; });
-  lb.init(tid);
+  lb.init(tid, n0, H);
 
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
   const int K = (int)(kend - kbeg);
-  main_loop<T, C>(
-      la, lb, [&](auto&, unsigned char* tile, int k0) { la.dma(gr, tile, k0, K); },
-      [&](auto& g, unsigned char*, int k0) {
+  main_loop<T, C, OA, OB>(
+      [&](unsigned char* tile, int k0) { la.issue(gr, tile, k0, K); },
+      [&](unsigned char* tile, int k0) {
         // W rows of this k-tile: one descriptor per tile keeps offsets small.
         const int64_t r0 = kbeg + k0;
         const int64_t nr = kend_w - r0 < KT<T>::BK ? kend_w - r0 : KT<T>::BK;
         const __amdgpu_buffer_rsrc_t wr =
             make_rsrc(W + r0 * H, nr > 0 ? (uint64_t)nr * H * sizeof(S) : 0);
-        lb.load(g, wr, 0,
-                [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * w_row_bytes : kOOB; }, n0, H);
+        lb.issue(wr, tile, 0,
+                 [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * w_row_bytes : kOOB; });
       },
       K > 0 ? (K + KT<T>::BK - 1) / KT<T>::BK : 0, smem_raw, wm, wn, lane, acc);
 
@@ -667,7 +677,7 @@ __device__ __forceinline__ void rmw8(void* dW, int64_t o, float (&v)[8], bool ac
 template <class T, class C, class D>
 __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
   typedef typename T::storage S;
-  typedef KColsLoader<T, C::BM, C::NT> OA;
+  typedef DmaCols<T, C::BM, C::NT / 64> OA;
   typedef DmaRows<T, C::BN, C::NT / 64> OB;
   extern __shared__ __align__(16) unsigned char smem_raw[];
 
@@ -692,23 +702,20 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
       make_rsrc(XcT + (int64_t)n0 * a.ldx, (uint64_t)xt_rows * a.ldx * sizeof(S));
   OA la;
   OB lb;
-  la.init(tid);
+  la.init(tid, (int)m0, (int)a.ldz);
   lb.init(tid, [&](int r) -> uint32_t { return r < xt_rows ? (uint32_t)r * xt_row_bytes : kOOB; });
-  const int ldz_cols = (int)a.ldz;
 
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
-  main_loop<T, C>(
-      la, lb,
-      [&](auto& g, unsigned char*, int k0) {
+  main_loop<T, C, OA, OB>(
+      [&](unsigned char* tile, int k0) {
         const int nr = a.rows - k0 < KT<T>::BK ? a.rows - k0 : KT<T>::BK;
         const __amdgpu_buffer_rsrc_t gr =
             make_rsrc(G + (int64_t)k0 * a.ldz, nr > 0 ? (uint64_t)nr * a.ldz * sizeof(S) : 0);
-        la.load(g, gr, 0,
-                [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * gz_bytes : kOOB; },
-                (int)m0, ldz_cols);
+        la.issue(gr, tile, 0,
+                 [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * gz_bytes : kOOB; });
       },
-      [&](auto&, unsigned char* tile, int k0) { lb.dma(xr, tile, k0, a.rows); },
+      [&](unsigned char* tile, int k0) { lb.issue(xr, tile, k0, a.rows); },
       (a.rows + KT<T>::BK - 1) / KT<T>::BK, smem_raw, wm, wn, lane, acc);
 
   const float sc = upstream_scale(a.grad_output, a.inv_n, a.reduction);
@@ -738,9 +745,9 @@ static hipError_t allow_lds(K kernel, size_t bytes) {
 template <class T, class C>
 struct LogitsSmem : Smem<C, DmaRows<T, C::BM, C::NT / 64>, DmaRows<T, C::BN, C::NT / 64>> {};
 template <class T, class C>
-struct DxSmem : Smem<C, DmaRows<T, C::BM, C::NT / 64>, KColsLoader<T, C::BN, C::NT>> {};
+struct DxSmem : Smem<C, DmaRows<T, C::BM, C::NT / 64>, DmaCols<T, C::BN, C::NT / 64>> {};
 template <class T, class C>
-struct DwSmem : Smem<C, KColsLoader<T, C::BM, C::NT>, DmaRows<T, C::BN, C::NT / 64>> {};
+struct DwSmem : Smem<C, DmaCols<T, C::BM, C::NT / 64>, DmaRows<T, C::BN, C::NT / 64>> {};
 
 template <class T, class C>
 static hipError_t launch_logits_t(const LogitsArgs& a, hipStream_t st) {
