@@ -38,12 +38,16 @@ typedef Cfg<256, 256> Big;
 typedef Cfg<128, 128> Small;
 
 // k-tile geometry: every LDS row of a k-contiguous tile holds kKBytes bytes
-// of k (BK = 64 bf16/fp16, 32 fp32), and tiles rotate through kStages LDS
-// buffers so that each one's loads have kStages - 1 k-tiles of MFMA work to
-// arrive in.  (Measured on MI355X: 128-byte rows with two stages beat
-// 64-byte rows with two to four stages.)
+// of k (BK = 64 bf16/fp16, 32 fp32).  (Measured on MI355X: 128-byte rows
+// beat 64-byte rows, whose extra barriers cost more than their extra stages
+// gain.)
 constexpr int kKBytes = 128;
-constexpr int kStages = 2;
+// LDS stages per operand (2 or 3; at most one operand with 3), per kernel.
+// A tile is needed S - 1 iterations after its loads are issued, so a third
+// stage doubles the time that operand's loads have to arrive.
+constexpr int kLogitsStagesA = 2, kLogitsStagesB = 2;
+constexpr int kDxStagesA = 2, kDxStagesB = 2;
+constexpr int kDwStagesA = 2, kDwStagesB = 2;
 
 template <class T>
 struct KT {
@@ -66,11 +70,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,
                                            0x00020000);
 }
-// 16 bytes per lane straight into LDS: lane i of the wave writes lds + 16 i.
+// 16 bytes per lane straight into LDS: lane i of the wave writes lds + 16 i
+// (M0 holds the wave's LDS base).  Issued from inline assembly on purpose:
+// the compiler cannot tell these LDS writes apart from the fragment reads of
+// the stage being multiplied, and would wait for every load in flight before
+// those reads, serialising the pipeline.  The k loop's own wait (vmcnt, then
+// a barrier) orders each stage's loads before its reads.
 __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                                unsigned char* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :
+               : "v"(off), "s"(base), "s"(r)
+               : "memory", "m0");
 }
 
 // Wait until at most `VM` vector-memory loads of this wave are outstanding
@@ -248,15 +261,18 @@ struct DmaCols {
   }
 };
 
-// Dynamic LDS of a kernel: kStages stages of (A tile, B tile), or the
-// epilogue's staging area (WTM x (BN + 4) fp32), whichever is larger.
-template <class C, class OA, class OB>
+// Dynamic LDS of a kernel: SA stages of the A tile and SB of the B tile,
+// or, after the main loop, the epilogue's staging area (WTM x (BN + 4) fp32)
+// plus EXTRA bytes, whichever is larger.
+template <class C, class OA, class OB, int SA, int SB, size_t EXTRA = 0>
 struct Smem {
-  static constexpr size_t STAGE = OA::TILE_BYTES + OB::TILE_BYTES;
-  static constexpr size_t OPERANDS = kStages * STAGE;
+  static_assert(SA >= 2 && SB >= 2, "at least two stages per operand");
+  static constexpr size_t B_OFS = (size_t)SA * OA::TILE_BYTES;
+  static constexpr size_t OPERANDS = B_OFS + (size_t)SB * OB::TILE_BYTES;
   static constexpr size_t EPI = (size_t)C::WTM * (C::BN + 4) * sizeof(float);
-  static constexpr size_t BYTES = OPERANDS > EPI ? OPERANDS : EPI;
-  static constexpr int VMEM_PER_TILE = OA::NI + OB::NI;
+  static constexpr size_t EPI_ALL = EPI + EXTRA;
+  static constexpr size_t BYTES = OPERANDS > EPI_ALL ? OPERANDS : EPI_ALL;
+  static_assert(BYTES <= 160 * 1024, "gfx950 LDS per workgroup");
 };
 
 // Fragment address helpers: a RowSwz operand is addressed by its row, a
@@ -346,40 +362,53 @@ __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned
   }
 }
 
-// The k loop shared by the three kernels: kStages LDS stages.  Before tile t
-// is multiplied, each wave waits until its own loads of tile t are done
-// (loads of the next kStages - 2 tiles may still be in flight) and meets the
-// other waves; then the loads of tile t + kStages - 1 go into the stage that
-// tile t - 1 used, which every wave has finished reading.
+// The k loop shared by the three kernels.  Operand X's k-tile j lives in
+// its stage j % SX and is loaded LX = SX - 1 iterations before it is
+// multiplied: iteration i issues A's tile i + LA and B's tile i + LB, into
+// the stages of tile i - 1, the operand with the shorter lead first.  Each
+// iteration first waits until this wave's loads of tile t are done (vector
+// loads complete in issue order, so it waits until no more than the loads
+// issued after them are outstanding) and meets the other waves, so that
+// every wave's loads of tile t have landed and every wave has finished
+// tile t - 1.
 //   ia(tile, k0) / ib(tile, k0): issue operand A's / B's k-tile at k0 into `tile`.
-template <class T, class C, class OA, class OB, class IA, class IB>
+template <class T, class C, class OA, class OB, int SA, int SB, class IA, class IB>
 __device__ __forceinline__ void main_loop(IA ia, IB ib, int nk, unsigned char* smem, int wm, int wn,
                                           int lane, f32x16_t (&acc)[C::FM][C::FN]) {
-  typedef typename OA::Layout LA;
-  typedef typename OB::Layout LB;
+  typedef typename OA::Layout LA_;
+  typedef typename OB::Layout LB_;
+  typedef Smem<C, OA, OB, SA, SB> SM;
   constexpr int BK = KT<T>::BK;
-  constexpr size_t ST = Smem<C, OA, OB>::STAGE;
-  constexpr int VM = (kStages - 2) * Smem<C, OA, OB>::VMEM_PER_TILE;
+  constexpr int LA = SA - 1, LB = SB - 1;
+  constexpr int LEAD = LA > LB ? LA : LB;
+  constexpr int PER_IT = OA::NI + OB::NI;
+  // loads issued after the later of A's and B's tile t
+  constexpr int AFTER = LA == LB ? (LA - 1) * PER_IT
+                        : LA > LB ? OA::NI + (LB - 1) * PER_IT
+                                  : OB::NI + (LA - 1) * PER_IT;
+  static_assert(AFTER < 64, "vmcnt range");
+  auto issue = [&](int i) {  // the loads of iteration i (may be negative: prologue)
+    const int ja = i + LA, jb = i + LB;
+    const bool da = ja >= 0 && ja < nk, db = jb >= 0 && jb < nk;
+    if constexpr (LA <= LB) {
+      if (da) ia(smem + (ja % SA) * OA::TILE_BYTES, ja * BK);
+      if (db) ib(smem + SM::B_OFS + (jb % SB) * OB::TILE_BYTES, jb * BK);
+    } else {
+      if (db) ib(smem + SM::B_OFS + (jb % SB) * OB::TILE_BYTES, jb * BK);
+      if (da) ia(smem + (ja % SA) * OA::TILE_BYTES, ja * BK);
+    }
+  };
   if (nk <= 0) return;
 #pragma unroll
-  for (int j = 0; j < kStages - 1; ++j)
-    if (j < nk) {
-      ia(smem + j * ST, j * BK);
-      ib(smem + j * ST + OA::TILE_BYTES, j * BK);
-    }
+  for (int i = -LEAD; i < 0; ++i) issue(i);
   for (int t = 0; t < nk; ++t) {
-    if (t + kStages - 2 < nk)
-      wait_and_barrier<VM>();
+    if (AFTER > 0 && t - 1 + LEAD < nk)
+      wait_and_barrier<AFTER>();
     else
       wait_and_barrier<0>();
-    const int tn = t + kStages - 1;
-    if (tn < nk) {
-      unsigned char* st = smem + (tn % kStages) * ST;
-      ia(st, tn * BK);
-      ib(st + OA::TILE_BYTES, tn * BK);
-    }
-    const unsigned char* cur = smem + (t % kStages) * ST;
-    mma_tile<T, C, LA, LB>(cur, cur + OA::TILE_BYTES, wm, wn, lane, acc);
+    issue(t);
+    mma_tile<T, C, LA_, LB_>(smem + (t % SA) * OA::TILE_BYTES,
+                             smem + SM::B_OFS + (t % SB) * OB::TILE_BYTES, wm, wn, lane, acc);
   }
   wait_and_barrier<0>();
 }
@@ -487,6 +516,21 @@ __device__ __forceinline__ float upstream_scale(const float* grad_output, float 
   return reduction == 0 ? g * inv_n : g;
 }
 
+// Tile coordinates of linear block id `lin` in a grid of `nr` x `nc` tiles,
+// walked in groups of `g` tile rows: within a group the row index varies
+// fastest, so consecutive blocks (which run together on one XCD) share
+// column tiles, and a group covers every column before the next begins.
+__device__ __forceinline__ void grouped_tile(int lin, int nr, int nc, int g, int& tr, int& tc) {
+  const int per_group = g * nc;
+  const int grp = lin / per_group;
+  const int first = grp * g;
+  const int gsz = nr - first < g ? nr - first : g;
+  const int r = lin - grp * per_group;
+  tr = first + r % gsz;
+  tc = r / gsz;
+}
+constexpr int kLogitsGroupM = 4, kDxGroupM = 4, kDwGroupN = 8;
+
 // ---------------------------------------------------------------------------
 // Logits: slab[m, n] = X[idx[m], :] . W[n, :], plus per-(row, wave column
 // block) running max and sum of exp, and the target logit in fp32.
@@ -496,13 +540,14 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   typedef typename T::storage S;
   typedef DmaRows<T, C::BM, C::NT / 64> OA;
   typedef DmaRows<T, C::BN, C::NT / 64> OB;
+  typedef Smem<C, OA, OB, kLogitsStagesA, kLogitsStagesB, C::BM * sizeof(int64_t)> SM;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ int64_t tgt_s[C::BM];
 
   const int tiles_m = (a.rows + C::BM - 1) / C::BM;
   const int tiles_n = (int)((a.V + C::BN - 1) / C::BN);
   const int lin = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-  const int tm = lin % tiles_m, tn = lin / tiles_m;  // M fastest: blocks sharing a W tile are adjacent
+  int tm, tn;  // M fastest within a group: blocks sharing a W tile are adjacent
+  grouped_tile(lin, tiles_m, tiles_n, kLogitsGroupM, tm, tn);
   const int m0 = tm * C::BM;
   const int64_t n0 = (int64_t)tn * C::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -510,10 +555,6 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
 
   const S* X = static_cast<const S*>(a.X);
   const S* W = static_cast<const S*>(a.W);
-  for (int m = tid; m < C::BM; m += C::NT) {
-    const int gm = m0 + m;
-    tgt_s[m] = gm < a.rows ? a.targets[a.idx[gm]] : -1;
-  }
 
   // X: gathered rows anywhere in [BT, H]; W: this tile's rows [n0, n0 + BN).
   const uint32_t row_bytes = (uint32_t)a.H * (uint32_t)sizeof(S);
@@ -531,7 +572,7 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
   const int K = (int)a.H;
-  main_loop<T, C, OA, OB>(
+  main_loop<T, C, OA, OB, kLogitsStagesA, kLogitsStagesB>(
       [&](unsigned char* tile, int k0) { la.issue(xr, tile, k0, K); },
       [&](unsigned char* tile, int k0) { lb.issue(wr, tile, k0, K); },
       (K + KT<T>::BK - 1) / KT<T>::BK, smem_raw, wm, wn, lane, acc);
@@ -540,6 +581,14 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   // the sum of exp(z - max) in fp32.  Both tile shapes reduce a 64-column
   // block the same way (8 lanes x 8 values), so a row's log-sum-exp does not
   // depend on the chunking.
+  // The block's target columns, after the staging area (the operand stages
+  // are free once the main loop is done; the epilogue's first barrier
+  // publishes them).
+  int64_t* tgt_s = reinterpret_cast<int64_t*>(smem_raw + SM::EPI);
+  for (int m = tid; m < C::BM; m += C::NT) {
+    const int gm = m0 + m;
+    tgt_s[m] = gm < a.rows ? a.targets[a.idx[gm]] : -1;
+  }
   S* slab = static_cast<S*>(a.slab);
   float2* stats = reinterpret_cast<float2*>(a.stats);
   staged_epilogue<C>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
@@ -583,7 +632,8 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
   const int lin = xcd_remap(blockIdx.x, per_split * a.splits);
   const int split = lin / per_split;
   const int rem = lin % per_split;
-  const int tm = rem % tiles_m, tn = rem / tiles_m;
+  int tm, tn;
+  grouped_tile(rem, tiles_m, tiles_n, kDxGroupM, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -610,7 +660,7 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
   const int K = (int)(kend - kbeg);
-  main_loop<T, C, OA, OB>(
+  main_loop<T, C, OA, OB, kDxStagesA, kDxStagesB>(
       [&](unsigned char* tile, int k0) { la.issue(gr, tile, k0, K); },
       [&](unsigned char* tile, int k0) {
         // W rows of this k-tile: one descriptor per tile keeps offsets small.
@@ -684,7 +734,8 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
   const int tiles_m = (int)((a.V + C::BM - 1) / C::BM);
   const int tiles_n = (int)((a.H + C::BN - 1) / C::BN);
   const int lin = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-  const int tn = lin % tiles_n, tm = lin / tiles_n;  // N fastest: blocks sharing a G tile are adjacent
+  int tm, tn;  // N fastest within a group: blocks sharing a G tile are adjacent
+  grouped_tile(lin, tiles_n, tiles_m, kDwGroupN, tn, tm);
   const int64_t m0 = (int64_t)tm * C::BM;
   const int n0 = tn * C::BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -707,7 +758,7 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
 
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
-  main_loop<T, C, OA, OB>(
+  main_loop<T, C, OA, OB, kDwStagesA, kDwStagesB>(
       [&](unsigned char* tile, int k0) {
         const int nr = a.rows - k0 < KT<T>::BK ? a.rows - k0 : KT<T>::BK;
         const __amdgpu_buffer_rsrc_t gr =
@@ -743,11 +794,14 @@ static hipError_t allow_lds(K kernel, size_t bytes) {
 }
 
 template <class T, class C>
-struct LogitsSmem : Smem<C, DmaRows<T, C::BM, C::NT / 64>, DmaRows<T, C::BN, C::NT / 64>> {};
+struct LogitsSmem : Smem<C, DmaRows<T, C::BM, C::NT / 64>, DmaRows<T, C::BN, C::NT / 64>,
+                         kLogitsStagesA, kLogitsStagesB, C::BM * sizeof(int64_t)> {};
 template <class T, class C>
-struct DxSmem : Smem<C, DmaRows<T, C::BM, C::NT / 64>, DmaCols<T, C::BN, C::NT / 64>> {};
+struct DxSmem : Smem<C, DmaRows<T, C::BM, C::NT / 64>, DmaCols<T, C::BN, C::NT / 64>,
+                     kDxStagesA, kDxStagesB> {};
 template <class T, class C>
-struct DwSmem : Smem<C, DmaCols<T, C::BM, C::NT / 64>, DmaRows<T, C::BN, C::NT / 64>> {};
+struct DwSmem : Smem<C, DmaCols<T, C::BM, C::NT / 64>, DmaRows<T, C::BN, C::NT / 64>,
+                     kDwStagesA, kDwStagesB> {};
 
 template <class T, class C>
 static hipError_t launch_logits_t(const LogitsArgs& a, hipStream_t st) {
