@@ -48,6 +48,9 @@ constexpr int kKBytes = 128;
 constexpr int kLogitsStagesA = 2, kLogitsStagesB = 2;
 constexpr int kDxStagesA = 2, kDxStagesB = 2;
 constexpr int kDwStagesA = 2, kDwStagesB = 2;
+// Parts each k-tile's loads are split into, spread over the k-steps of the
+// previous tile's MFMA work (1: all issued after the first k-step).
+constexpr int kLogitsParts = 1, kDxParts = 2, kDwParts = 4;
 
 template <class T>
 struct KT {
@@ -65,10 +68,18 @@ struct KT {
 // ---------------------------------------------------------------------------
 constexpr uint32_t kOOB = 0xfffffff0u;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+// Buffer descriptor (V#) in four wave-uniform words: base address, stride 0,
+// size in bytes (reads at or past it return zero), raw-buffer format flags.
+typedef int32_t desc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ desc_t make_rsrc(const void* base, uint64_t bytes) {
   const uint32_t n = bytes > 0x7ffffff0ull ? 0x7ffffff0u : (uint32_t)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,
-                                           0x00020000);
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  desc_t d;
+  d[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b);
+  d[1] = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(b >> 32) & 0xffffu));
+  d[2] = __builtin_amdgcn_readfirstlane((int32_t)n);
+  d[3] = 0x00020000;
+  return d;
 }
 // 16 bytes per lane straight into LDS: lane i of the wave writes lds + 16 i
 // (M0 holds the wave's LDS base).  Issued from inline assembly on purpose:
@@ -76,14 +87,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // the stage being multiplied, and would wait for every load in flight before
 // those reads, serialising the pipeline.  The k loop's own wait (vmcnt, then
 // a barrier) orders each stage's loads before its reads.
-__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t off,
-                                               unsigned char* lds) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds);
+__device__ __forceinline__ void buf_load16_lds(desc_t r, uint32_t off, unsigned char* lds) {
+  // A generic pointer into LDS is the LDS aperture base plus the LDS offset,
+  // so its low 32 bits are the offset M0 wants.
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
                :
                : "v"(off), "s"(base), "s"(r)
-               : "memory", "m0");
+               : "memory");
 }
 
 // Wait until at most `VM` vector-memory loads of this wave are outstanding
@@ -205,9 +216,14 @@ struct DmaRows {
       kc_el[i] = ((lane % CPR) ^ Layout::swz(row)) * T::vec;
     }
   }
-  __device__ void issue(__amdgpu_buffer_rsrc_t rs, unsigned char* tile, int k0, int kend) const {
+  // Part `part` of P: the instructions i with i * P / NI == part (P parts
+  // spread the tile's loads over the P k-steps of the previous tile).
+  template <int P>
+  __device__ void issue(desc_t rs, unsigned char* tile, int k0, int kend,
+                        int part) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
+      if (i * P / NI != part) continue;
       const int k = k0 + kc_el[i];
       buf_load16_lds(rs,
                      (k < kend && roff[i] != kOOB) ? roff[i] + (uint32_t)k * (uint32_t)sizeof(S)
@@ -249,11 +265,12 @@ struct DmaCols {
       cofs[i] = c < cend ? (uint32_t)c * (uint32_t)sizeof(S) : kOOB;
     }
   }
-  template <class KFn>
-  __device__ void issue(__amdgpu_buffer_rsrc_t rs, unsigned char* tile, int k0,
-                        KFn rowoff) const {
+  template <int P, class KFn>
+  __device__ void issue(desc_t rs, unsigned char* tile, int k0, KFn rowoff,
+                        int part) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
+      if (i * P / NI != part) continue;
       const uint32_t ro = rowoff(k0 + krow[i]);
       buf_load16_lds(rs, (ro != kOOB && cofs[i] != kOOB) ? ro + cofs[i] : kOOB,
                      tile + (wave + i * NWAVES) * 1024);
@@ -313,10 +330,10 @@ struct PinInterleave<NR, NM, NR> {
   __device__ static void run() {}
 };
 
-template <class T, class C, class LA, class LB>
+template <class T, class C, class LA, class LB, class DMA>
 __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned char* Bb,
                                          int wm, int wn, int lane,
-                                         f32x16_t (&acc)[C::FM][C::FN]) {
+                                         f32x16_t (&acc)[C::FM][C::FN], DMA dma) {
   constexpr int STEPS = KT<T>::STEPS;
   if constexpr (sizeof(typename T::storage) == 2) {
     u32x4_t fa[2][C::FM], fb[2][C::FN];
@@ -334,6 +351,7 @@ __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) T::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+      dma(s);
     }
     // reads per step: one per RowSwz fragment, two per ColSwz fragment
     constexpr int NR = C::FM * (IsCol<LA>::value ? 2 : 1) + C::FN * (IsCol<LB>::value ? 2 : 1);
@@ -358,6 +376,7 @@ __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) T::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+      dma(s);
     }
   }
 }
@@ -365,20 +384,28 @@ __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned
 // The k loop shared by the three kernels.  Operand X's k-tile j lives in
 // its stage j % SX and is loaded LX = SX - 1 iterations before it is
 // multiplied: iteration i issues A's tile i + LA and B's tile i + LB, into
-// the stages of tile i - 1, the operand with the shorter lead first.  Each
+// the stages of tile i - 1, the operand with the shorter lead first.  The
+// loads are spread over the k-steps of the MFMA work (part s after step s),
+// so that no wave stalls on a burst of loads queued behind the other waves'
+// before its first MFMA.  Tiles past the end are issued too, as loads that
+// read zeros into a free stage, which keeps the loop body branch-free.  Each
 // iteration first waits until this wave's loads of tile t are done (vector
 // loads complete in issue order, so it waits until no more than the loads
 // issued after them are outstanding) and meets the other waves, so that
 // every wave's loads of tile t have landed and every wave has finished
 // tile t - 1.
-//   ia(tile, k0) / ib(tile, k0): issue operand A's / B's k-tile at k0 into `tile`.
-template <class T, class C, class OA, class OB, int SA, int SB, class IA, class IB>
+//   ia(tile, k0, part) / ib(tile, k0, part): issue part `part` (of the
+//   k-steps per tile) of operand A's / B's k-tile at k0 into `tile`; a k0 at
+//   or past the end reads zeros.
+template <class T, class C, class OA, class OB, int SA, int SB, int P, class IA, class IB>
 __device__ __forceinline__ void main_loop(IA ia, IB ib, int nk, unsigned char* smem, int wm, int wn,
                                           int lane, f32x16_t (&acc)[C::FM][C::FN]) {
   typedef typename OA::Layout LA_;
   typedef typename OB::Layout LB_;
   typedef Smem<C, OA, OB, SA, SB> SM;
   constexpr int BK = KT<T>::BK;
+  constexpr int STEPS = KT<T>::STEPS;
+  static_assert(P >= 1 && STEPS % P == 0, "parts must divide the k-steps");
   constexpr int LA = SA - 1, LB = SB - 1;
   constexpr int LEAD = LA > LB ? LA : LB;
   constexpr int PER_IT = OA::NI + OB::NI;
@@ -387,28 +414,31 @@ __device__ __forceinline__ void main_loop(IA ia, IB ib, int nk, unsigned char* s
                         : LA > LB ? OA::NI + (LB - 1) * PER_IT
                                   : OB::NI + (LA - 1) * PER_IT;
   static_assert(AFTER < 64, "vmcnt range");
-  auto issue = [&](int i) {  // the loads of iteration i (may be negative: prologue)
+  auto tile_a = [&](int j) { return smem + (j % SA) * OA::TILE_BYTES; };
+  auto tile_b = [&](int j) { return smem + SM::B_OFS + (j % SB) * OB::TILE_BYTES; };
+  auto issue = [&](int i, int part) {  // part of the loads of iteration i
     const int ja = i + LA, jb = i + LB;
-    const bool da = ja >= 0 && ja < nk, db = jb >= 0 && jb < nk;
     if constexpr (LA <= LB) {
-      if (da) ia(smem + (ja % SA) * OA::TILE_BYTES, ja * BK);
-      if (db) ib(smem + SM::B_OFS + (jb % SB) * OB::TILE_BYTES, jb * BK);
+      if (ja >= 0) ia(tile_a(ja), ja * BK, part);
+      if (jb >= 0) ib(tile_b(jb), jb * BK, part);
     } else {
-      if (db) ib(smem + SM::B_OFS + (jb % SB) * OB::TILE_BYTES, jb * BK);
-      if (da) ia(smem + (ja % SA) * OA::TILE_BYTES, ja * BK);
+      if (jb >= 0) ib(tile_b(jb), jb * BK, part);
+      if (ja >= 0) ia(tile_a(ja), ja * BK, part);
     }
   };
   if (nk <= 0) return;
 #pragma unroll
-  for (int i = -LEAD; i < 0; ++i) issue(i);
+  for (int i = -LEAD; i < 0; ++i)
+#pragma unroll
+    for (int p = 0; p < P; ++p) issue(i, p);
   for (int t = 0; t < nk; ++t) {
     if (AFTER > 0 && t - 1 + LEAD < nk)
       wait_and_barrier<AFTER>();
     else
       wait_and_barrier<0>();
-    issue(t);
-    mma_tile<T, C, LA_, LB_>(smem + (t % SA) * OA::TILE_BYTES,
-                             smem + SM::B_OFS + (t % SB) * OB::TILE_BYTES, wm, wn, lane, acc);
+    mma_tile<T, C, LA_, LB_>(tile_a(t), tile_b(t), wm, wn, lane, acc, [&](int s) {
+      if (s % (STEPS / P) == 0) issue(t, s / (STEPS / P));
+    });
   }
   wait_and_barrier<0>();
 }
@@ -558,9 +588,9 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
 
   // X: gathered rows anywhere in [BT, H]; W: this tile's rows [n0, n0 + BN).
   const uint32_t row_bytes = (uint32_t)a.H * (uint32_t)sizeof(S);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint64_t)a.BT * a.H * sizeof(S));
+  const desc_t xr = make_rsrc(X, (uint64_t)a.BT * a.H * sizeof(S));
   const int64_t nrows_w = a.V - n0 < C::BN ? a.V - n0 : C::BN;
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + n0 * a.H, (uint64_t)nrows_w * a.H * sizeof(S));
+  const desc_t wr = make_rsrc(W + n0 * a.H, (uint64_t)nrows_w * a.H * sizeof(S));
   OA la;
   OB lb;
   la.init(tid, [&](int r) -> uint32_t {
@@ -572,9 +602,10 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
   const int K = (int)a.H;
-  main_loop<T, C, OA, OB, kLogitsStagesA, kLogitsStagesB>(
-      [&](unsigned char* tile, int k0) { la.issue(xr, tile, k0, K); },
-      [&](unsigned char* tile, int k0) { lb.issue(wr, tile, k0, K); },
+  constexpr int P = kLogitsParts;
+  main_loop<T, C, OA, OB, kLogitsStagesA, kLogitsStagesB, P>(
+      [&](unsigned char* tile, int k0, int p) { la.template issue<P>(xr, tile, k0, K, p); },
+      [&](unsigned char* tile, int k0, int p) { lb.template issue<P>(wr, tile, k0, K, p); },
       (K + KT<T>::BK - 1) / KT<T>::BK, smem_raw, wm, wn, lane, acc);
 
   // Epilogue: store the logits, and per (row, 64-column block) the max and
@@ -649,7 +680,7 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
   // W: rows [kbeg, kend_w), one descriptor per k-tile.
   const uint32_t gz_bytes = (uint32_t)a.ldz * (uint32_t)sizeof(S);
   const int g_rows = a.rows - m0 < C::BM ? a.rows - m0 : C::BM;
-  const __amdgpu_buffer_rsrc_t gr = make_rsrc(
+  const desc_t gr = make_rsrc(
       G + (int64_t)m0 * a.ldz + kbeg, ((uint64_t)g_rows * a.ldz - kbeg) * sizeof(S));
   const uint32_t w_row_bytes = (uint32_t)H * (uint32_t)sizeof(S);
   OA la;
@@ -660,16 +691,20 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
   const int K = (int)(kend - kbeg);
-  main_loop<T, C, OA, OB, kDxStagesA, kDxStagesB>(
-      [&](unsigned char* tile, int k0) { la.issue(gr, tile, k0, K); },
-      [&](unsigned char* tile, int k0) {
+  constexpr int P = kDxParts < KT<T>::STEPS ? kDxParts : KT<T>::STEPS;
+  main_loop<T, C, OA, OB, kDxStagesA, kDxStagesB, P>(
+      [&](unsigned char* tile, int k0, int p) { la.template issue<P>(gr, tile, k0, K, p); },
+      [&](unsigned char* tile, int k0, int p) {
         // W rows of this k-tile: one descriptor per tile keeps offsets small.
+        // (branch-free: a tile past the end gets an empty descriptor)
         const int64_t r0 = kbeg + k0;
-        const int64_t nr = kend_w - r0 < KT<T>::BK ? kend_w - r0 : KT<T>::BK;
-        const __amdgpu_buffer_rsrc_t wr =
-            make_rsrc(W + r0 * H, nr > 0 ? (uint64_t)nr * H * sizeof(S) : 0);
-        lb.issue(wr, tile, 0,
-                 [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * w_row_bytes : kOOB; });
+        const int64_t left = kend_w - r0;
+        const int nr = left <= 0 ? 0 : (left < KT<T>::BK ? (int)left : KT<T>::BK);
+        const desc_t wr =
+            make_rsrc(W + (left > 0 ? r0 : 0) * H, (uint32_t)nr * w_row_bytes);
+        lb.template issue<P>(
+            wr, tile, 0, [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * w_row_bytes : kOOB; },
+            p);
       },
       K > 0 ? (K + KT<T>::BK - 1) / KT<T>::BK : 0, smem_raw, wm, wn, lane, acc);
 
@@ -699,28 +734,75 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
 // The accumulator starts at zero and the destination is read only in the
 // epilogue, so no [V, H] temporary exists.
 // ---------------------------------------------------------------------------
-// Read-modify-write of 8 consecutive dW entries in the destination dtype D
-// (float, or the 16-bit operand type).
-template <class D>
-__device__ __forceinline__ void rmw8(void* dW, int64_t o, float (&v)[8], bool accumulate) {
-  if constexpr (std::is_same<D, float>::value) {
-    f32x4_t* p = reinterpret_cast<f32x4_t*>(static_cast<float*>(dW) + o);
-    f32x4_t lo{v[0], v[1], v[2], v[3]}, hi{v[4], v[5], v[6], v[7]};
-    if (accumulate) {
-      lo += p[0];
-      hi += p[1];
-    }
-    p[0] = lo;
-    p[1] = hi;
-  } else {
-    u32x4_t* p = reinterpret_cast<u32x4_t*>(static_cast<u16*>(dW) + o);
-    if (accumulate) {
-      float old[8];
-      unpack8<D>(*p, old);
+// The grad_weight epilogue: staged like staged_epilogue, but every value a
+// thread will add to is loaded before the pass's accumulators are staged,
+// so those loads' latency overlaps the staging instead of serialising with
+// the stores (the compiler cannot move a load of one piece above the store
+// of another).
+template <class C, class D>
+__device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[C::FM][C::FN],
+                                            int wm, int wn, int lane, int tid, void* dW,
+                                            int64_t m0, int n0, int64_t V, int H, float sc,
+                                            bool accumulate) {
+  constexpr int LS = Stage<C>::LS, SUBS = Stage<C>::SUBS;
+  constexpr int NQ = C::WTM * SUBS / C::NT;  // pieces per thread per pass
+  constexpr bool F32 = std::is_same<D, float>::value;
+  for (int p = 0; p < C::WAVES_M; ++p) {
+    u32x4_t old[NQ][F32 ? 2 : 1];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] += old[e];
+    for (int i = 0; i < NQ; ++i) {
+      const int q = tid + i * C::NT, lrow = q / SUBS, piece = q % SUBS;
+      const int64_t gm = m0 + p * C::WTM + lrow;
+      const int gn = n0 + piece * 8;
+      const bool live = accumulate && gm < V && gn < H;
+#pragma unroll
+      for (int h = 0; h < (F32 ? 2 : 1); ++h) {
+        old[i][h] = u32x4_t{0u, 0u, 0u, 0u};
+        if (live) {
+          if constexpr (F32)
+            old[i][h] = reinterpret_cast<const u32x4_t*>(static_cast<float*>(dW) + gm * H + gn)[h];
+          else
+            old[i][h] = *reinterpret_cast<const u32x4_t*>(static_cast<u16*>(dW) + gm * H + gn);
+        }
+      }
     }
-    *p = pack8<D>(v);
+    __syncthreads();
+    if (wm == p) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int col = wn * C::WTN + j * 32 + (lane & 31);
+            stage[row * LS + col] = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int q = tid + i * C::NT, lrow = q / SUBS, piece = q % SUBS;
+      const int64_t gm = m0 + p * C::WTM + lrow;
+      const int gn = n0 + piece * 8;
+      if (gm >= V || gn >= H) continue;
+      const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8);
+      const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8 + 4);
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if constexpr (F32) {
+        f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(dW) + gm * H + gn);
+        const f32x4_t o0 = __builtin_bit_cast(f32x4_t, old[i][0]);
+        const f32x4_t o1 = __builtin_bit_cast(f32x4_t, old[i][1]);
+        dst[0] = f32x4_t{v[0] * sc + o0[0], v[1] * sc + o0[1], v[2] * sc + o0[2], v[3] * sc + o0[3]};
+        dst[1] = f32x4_t{v[4] * sc + o1[0], v[5] * sc + o1[1], v[6] * sc + o1[2], v[7] * sc + o1[3]};
+      } else {
+        float o[8];
+        unpack8<D>(old[i][0], o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = v[e] * sc + o[e];
+        *reinterpret_cast<u32x4_t*>(static_cast<u16*>(dW) + gm * H + gn) = pack8<D>(v);
+      }
+    }
   }
 }
 
@@ -749,7 +831,7 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
   const uint32_t gz_bytes = (uint32_t)a.ldz * (uint32_t)sizeof(S);
   const uint32_t xt_row_bytes = (uint32_t)a.ldx * (uint32_t)sizeof(S);
   const int xt_rows = H - n0 < C::BN ? H - n0 : C::BN;
-  const __amdgpu_buffer_rsrc_t xr =
+  const desc_t xr =
       make_rsrc(XcT + (int64_t)n0 * a.ldx, (uint64_t)xt_rows * a.ldx * sizeof(S));
   OA la;
   OB lb;
@@ -758,28 +840,25 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
 
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
-  main_loop<T, C, OA, OB, kDwStagesA, kDwStagesB>(
-      [&](unsigned char* tile, int k0) {
-        const int nr = a.rows - k0 < KT<T>::BK ? a.rows - k0 : KT<T>::BK;
-        const __amdgpu_buffer_rsrc_t gr =
-            make_rsrc(G + (int64_t)k0 * a.ldz, nr > 0 ? (uint64_t)nr * a.ldz * sizeof(S) : 0);
-        la.issue(gr, tile, 0,
-                 [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * gz_bytes : kOOB; });
+  constexpr int P = kDwParts < KT<T>::STEPS ? kDwParts : KT<T>::STEPS;
+  main_loop<T, C, OA, OB, kDwStagesA, kDwStagesB, P>(
+      [&](unsigned char* tile, int k0, int p) {
+        // (branch-free: a tile past the end gets an empty descriptor)
+        const int left = a.rows - k0;
+        const int nr = left <= 0 ? 0 : (left < KT<T>::BK ? left : KT<T>::BK);
+        const desc_t gr =
+            make_rsrc(G + (int64_t)(left > 0 ? k0 : 0) * a.ldz, (uint32_t)nr * gz_bytes);
+        la.template issue<P>(
+            gr, tile, 0, [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * gz_bytes : kOOB; },
+            p);
       },
-      [&](unsigned char* tile, int k0) { lb.issue(xr, tile, k0, a.rows); },
+      [&](unsigned char* tile, int k0, int p) { lb.template issue<P>(xr, tile, k0, a.rows, p); },
       (a.rows + KT<T>::BK - 1) / KT<T>::BK, smem_raw, wm, wn, lane, acc);
 
   const float sc = upstream_scale(a.grad_output, a.inv_n, a.reduction);
   const bool accumulate = a.accumulate != 0;
-  staged_epilogue<C>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
-                     [&](int brow, int bcol, float (&v)[8]) {
-    const int64_t gm = m0 + brow;
-    const int gn = n0 + bcol;
-    if (gm >= a.V || gn >= H) return;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= sc;
-    rmw8<D>(a.dW, gm * H + gn, v, accumulate);
-  });
+  dw_epilogue<C, D>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid, a.dW, m0, n0, a.V,
+                    H, sc, accumulate);
 }
 
 // ---------------------------------------------------------------------------
