@@ -64,7 +64,7 @@ def parse():
     p.add_argument("--workload", default="llama3_8b_lm_head", choices=sorted(WORKLOADS))
     p.add_argument("--extra", default="llama3_8b_lm_head_c256",
                    help="comma-separated extra workloads reported under 'extra' ('' for none)")
-    p.add_argument("--cpu-rows", type=int, default=16, help="rows in the oracle's timed sample")
+    p.add_argument("--cpu-rows", type=int, default=256, help="rows in the oracle's timed sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run plain 1 GiB device copies (reference for HBM byte counters)")
