@@ -62,6 +62,10 @@ def _bind(path: str):
     lib.oracle_dx_rows.restype = I
     lib.oracle_dw_rows.argtypes = [P, P, P, I64, I64, I64, I, P, I64, P, I64, P, P]
     lib.oracle_dw_rows.restype = I
+    D = ctypes.c_double
+    lib.oracle_flce_ex.argtypes = [P, P, P, P, I64, I64, I64, I64, I, P, D, I, P, P, P, P, P, P,
+                                   P]
+    lib.oracle_flce_ex.restype = I
     return lib
 
 
@@ -146,6 +150,47 @@ def flce(X, W, targets, *, ignore_index: int = -100, reduction: str = "mean",
         raise RuntimeError(f"oracle_flce failed with {rc}")
     return dict(loss=loss if reduction == "none" else float(loss[0]), dX=dX, dW=dW, lse=lse,
                 n_valid=int(n[0]))
+
+
+def flce_ex(X, W, targets, *, bias=None, z_loss_scale: float = 0.0, ignore_index: int = -100,
+            reduction: str = "mean", grad_output=None, dW_init=None, db_init=None,
+            grads: bool = True):
+    """The method with bias, z-loss and per-token outputs (small cases only).
+
+    Returns loss, z_loss, accuracy (scalars for mean/sum, [BT] for none),
+    predicted [BT] (int64, -1 at ignored rows) and, with ``grads``, dX, dW and
+    grad_bias (when a bias is given).  ``dW_init`` / ``db_init`` turn the
+    weight / bias gradients into accumulations onto those values.
+    """
+    Xd, Wd, t = widen(X), widen(W), _i64(targets)
+    BT, H = Xd.shape
+    V = Wd.shape[0]
+    bd = None if bias is None else widen(bias).reshape(-1)
+    g = _grad(grad_output, reduction, BT)
+    nout = BT if reduction == "none" else 1
+    loss = np.zeros(nout)
+    zl = np.zeros(nout)
+    acc = np.zeros(nout)
+    pred = np.zeros(max(BT, 1), dtype=np.int64)
+    accumulate = dW_init is not None or db_init is not None
+    dX = np.zeros((BT, H)) if grads else None
+    dW = None
+    db = None
+    if grads:
+        dW = np.zeros((V, H)) if dW_init is None else widen(dW_init).copy()
+        if bd is not None:
+            db = np.zeros(V) if db_init is None else widen(db_init).reshape(-1).copy()
+    rc = _load().oracle_flce_ex(_p(Xd), _p(Wd), _p(bd), _p(t), BT, H, V, ignore_index,
+                                REDUCTIONS[reduction], _p(g), float(z_loss_scale),
+                                int(accumulate), _p(loss), _p(dX), _p(dW), _p(db), _p(zl),
+                                _p(acc), _p(pred))
+    if rc == E_TARGET:
+        raise OracleTargetError("labelled target outside [0, V)")
+    if rc != 0:
+        raise RuntimeError(f"oracle_flce_ex failed with {rc}")
+    red = (lambda a: a) if reduction == "none" else (lambda a: float(a[0]))
+    return dict(loss=red(loss), z_loss=red(zl), accuracy=red(acc), predicted=pred[:BT],
+                dX=dX, dW=dW, grad_bias=db)
 
 
 def lse(X, W, targets, *, ignore_index: int = -100) -> np.ndarray:

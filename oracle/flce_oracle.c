@@ -341,3 +341,117 @@ int oracle_dw_rows(const double* X, const double* W, const int64_t* t, int64_t B
   }
   return err ? ORACLE_E_MEM : ORACLE_OK;
 }
+
+/*
+ * The method with its optional parts, for small cases (the whole gradient
+ * matrix G [BT, V] is held in memory).
+ *
+ *   bias (PR #1554, Tests: the ignored-row cases run with bias on and off):
+ *       z[i,v] = sum_k X[i,k] W[v,k] + b[v];  grad_bias[v] = sum_i G[i,v].
+ *   per-token outputs (PR #1554, Details item 1 and Tests: per-token loss,
+ *   z-loss, accuracy and predicted token; ignored rows get 0, 0, 0 and -1).
+ *   The pages do not define them; the readings used here are:
+ *       predicted_i = argmax_v z[i,v], the lowest such v on ties;
+ *       accuracy_i  = 1 if predicted_i == t_i else 0;
+ *       z-loss_i    = lse_i^2, the squared log-partition function.
+ *   z-loss coefficient lam >= 0 (reading: when non-zero the term lam*lse_i^2
+ *   joins the per-row loss and the gradient follows it):
+ *       loss_i = lse_i - z[i,t_i] + lam * lse_i^2
+ *       G[i,v] = s_i * ((1 + 2 lam lse_i) softmax(z_i)_v - [v == t_i])
+ *   Reduced per-token outputs (mean / sum) follow the loss: the sum over
+ *   labelled rows, divided by N for mean (0 when N == 0).
+ *
+ * Arguments as oracle_flce, plus:
+ *   bias [V] or NULL; lam; grad_bias [V] or NULL (overwritten, or added to
+ *   when accumulate != 0); zl, acc: NULL or [1] (mean/sum) / [BT] (none);
+ *   pred: NULL or [BT].  dX, dW may be NULL (not computed).
+ */
+int oracle_flce_ex(const double* X, const double* W, const double* bias, const int64_t* t,
+                   int64_t BT, int64_t H, int64_t V, int64_t ignore_index, int reduction,
+                   const double* grad_output, double lam, int accumulate, double* loss,
+                   double* dX, double* dW, double* grad_bias, double* zl, double* acc,
+                   int64_t* pred) {
+  if (BT < 0 || H < 1 || V < 1 || lam < 0.0) return ORACLE_E_ARG;
+  if (reduction < ORACLE_MEAN || reduction > ORACLE_NONE) return ORACLE_E_ARG;
+  const size_t nb = (size_t)(BT > 0 ? BT : 1);
+  int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * nb);
+  double* G = (double*)calloc(nb * (size_t)V, sizeof(double));
+  double* z = (double*)malloc(sizeof(double) * (size_t)V);
+  double* lrow = (double*)calloc(nb, sizeof(double));
+  double* zrow = (double*)calloc(nb, sizeof(double));
+  double* arow = (double*)calloc(nb, sizeof(double));
+  int rc = ORACLE_OK;
+  int64_t N = 0;
+  if (!idx || !G || !z || !lrow || !zrow || !arow) rc = ORACLE_E_MEM;
+  if (rc == ORACLE_OK) rc = oracle_compact(t, BT, V, ignore_index, idx, &N);
+  if (rc != ORACLE_OK) {
+    free(idx); free(G); free(z); free(lrow); free(zrow); free(arow);
+    return rc;
+  }
+  if (pred)
+    for (int64_t i = 0; i < BT; ++i) pred[i] = -1;
+
+  /* Rows: logits with bias, log-sum-exp, per-token outputs, G. */
+  for (int64_t n = 0; n < N; ++n) {
+    const int64_t i = idx[n];
+    logits_row(X, W, H, V, i, z);
+    if (bias)
+      for (int64_t v = 0; v < V; ++v) z[v] += bias[v];
+    const double l = logsumexp_row(z, V);
+    int64_t am = 0;
+    for (int64_t v = 1; v < V; ++v)
+      if (z[v] > z[am]) am = v;
+    lrow[i] = l - z[t[i]] + lam * l * l;
+    zrow[i] = l * l;
+    arow[i] = (am == t[i]) ? 1.0 : 0.0;
+    if (pred) pred[i] = am;
+    const double s = row_scale(reduction, grad_output, i, N);
+    for (int64_t v = 0; v < V; ++v)
+      G[i * V + v] = s * ((1.0 + 2.0 * lam * l) * exp(z[v] - l) - (v == t[i] ? 1.0 : 0.0));
+  }
+
+  /* Loss and per-token outputs: per row (none), or reduced over labelled rows. */
+  if (reduction == ORACLE_NONE) {
+    for (int64_t i = 0; i < BT; ++i) {
+      loss[i] = lrow[i];
+      if (zl) zl[i] = zrow[i];
+      if (acc) acc[i] = arow[i];
+    }
+  } else {
+    double sl = 0.0, sz = 0.0, sa = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      sl += lrow[idx[n]];
+      sz += zrow[idx[n]];
+      sa += arow[idx[n]];
+    }
+    const double d = (reduction == ORACLE_MEAN) ? (N > 0 ? (double)N : 0.0) : 1.0;
+    loss[0] = d > 0.0 ? sl / d : 0.0;
+    if (zl) zl[0] = d > 0.0 ? sz / d : 0.0;
+    if (acc) acc[0] = d > 0.0 ? sa / d : 0.0;
+  }
+
+  /* grad_input = G W, grad_weight = G^T X, grad_bias = column sums of G;
+   * ignored rows of G are zero, so they add nothing. */
+  if (dX)
+    for (int64_t i = 0; i < BT; ++i)
+      for (int64_t k = 0; k < H; ++k) {
+        double a = 0.0;
+        for (int64_t v = 0; v < V; ++v) a += G[i * V + v] * W[v * H + k];
+        dX[i * H + k] = a;
+      }
+  if (dW)
+    for (int64_t v = 0; v < V; ++v)
+      for (int64_t k = 0; k < H; ++k) {
+        double a = 0.0;
+        for (int64_t i = 0; i < BT; ++i) a += G[i * V + v] * X[i * H + k];
+        dW[v * H + k] = accumulate ? dW[v * H + k] + a : a;
+      }
+  if (grad_bias)
+    for (int64_t v = 0; v < V; ++v) {
+      double a = 0.0;
+      for (int64_t i = 0; i < BT; ++i) a += G[i * V + v];
+      grad_bias[v] = accumulate ? grad_bias[v] + a : a;
+    }
+  free(idx); free(G); free(z); free(lrow); free(zrow); free(arow);
+  return ORACLE_OK;
+}
