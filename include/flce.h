@@ -143,6 +143,73 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
                  void* stream, flce_stats_t* stats);
 
 /*
+ * Optional parts of the method, for flce_fwd_bwd_ex.  A zero-filled struct,
+ * or NULL, gives exactly flce_fwd_bwd.
+ *
+ *   forward_only  1: the call computes the loss and the per-token outputs
+ *                 below and nothing else.  No gradient GEMM runs and the
+ *                 logits are never stored; dX, dW and grad_bias are not
+ *                 touched and may be NULL.  Serves the none reduction, whose
+ *                 per-token upstream gradient is only known in backward: the
+ *                 forward asks for the loss, and backward calls again with
+ *                 grad_output (PR #1554, Tests: the none reduction re-enters
+ *                 the chunk loop).
+ *   bias          [V] dtype, or NULL: every row's logits become
+ *                 z = X W^T + bias (PR #1554, Tests: bias on and off).
+ *   grad_bias     [V] accum_dtype, or NULL: the column sums of the logit
+ *                 gradient, scaled like dW; overwritten, or added to when
+ *                 accumulate_dw = 1.  Computed whenever given and not
+ *                 forward_only (frozen_weight does not affect it).
+ *   z_loss_scale  lam >= 0: the per-row loss gains lam * lse_i^2, where lse_i
+ *                 is the row's log-sum-exp, and the gradient follows it.  The
+ *                 pages name a per-token z-loss output without defining it;
+ *                 lse^2 with this optional coefficient is the reading taken.
+ *   z_loss        NULL, or lse_i^2 per labelled row: none -> [BT] (ignored
+ *                 rows 0); mean / sum -> [1], reduced like the loss.
+ *   accuracy      NULL, or 1 when the predicted token equals the target, else
+ *                 0: none -> [BT] (ignored rows 0); mean / sum -> [1], reduced
+ *                 like the loss (the fraction or the count of correct rows).
+ *   predicted     NULL, or [BT] int64: the lowest column holding the row's
+ *                 largest logit (fp32), -1 at ignored rows (PR #1554, Details
+ *                 item 1: ignored rows get 0 per-token loss, z-loss and
+ *                 accuracy and -1 as predicted token).
+ * Pointers are device pointers: bias and grad_bias 16-byte aligned,
+ * predicted 8-byte, z_loss and accuracy 4-byte.
+ */
+typedef struct {
+  int32_t forward_only;
+  const void* bias;
+  void* grad_bias;
+  float z_loss_scale;
+  float* z_loss;
+  float* accuracy;
+  int64_t* predicted;
+} flce_options_t;
+
+/* Workspace for flce_fwd_bwd_ex with these options; with opt NULL it equals
+ * flce_workspace_bytes.  A forward_only call needs no logits slab and far
+ * less; the per-token outputs and grad_bias add small per-call arrays.
+ * 0 when invalid. */
+size_t flce_workspace_bytes_ex(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,
+                               int64_t chunk_size, int32_t chunk_mem_const,
+                               const flce_options_t* opt);
+
+/*
+ * flce_fwd_bwd with the optional parts above; every other argument, the
+ * single host sync, the errors and the stream semantics are flce_fwd_bwd's.
+ * With forward_only, dX and dW may be NULL.  Invalid options (misaligned
+ * pointers, lam < 0 or not finite, forward_only not 0/1) return FLCE_E_ARG
+ * before any launch.  The workspace must hold flce_workspace_bytes_ex bytes.
+ */
+int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
+                    int64_t V, flce_dtype_t dtype, int64_t ignore_index,
+                    flce_reduction_t reduction, int64_t chunk_size, int32_t chunk_mem_const,
+                    flce_dtype_t accum_dtype, int32_t frozen_weight, int32_t accumulate_dw,
+                    const float* grad_output, float* loss, void* dX, void* dW, void* workspace,
+                    size_t workspace_bytes, void* stream, flce_stats_t* stats,
+                    const flce_options_t* opt);
+
+/*
  * dst[i] = scale * src[i], converted to dst_dtype (round to nearest even).
  * Serves the wrapper's two elementwise steps: the final cast of an fp32
  * grad_weight to the weight dtype (PR #1554, Tests: chunk storage is released
@@ -178,7 +245,8 @@ typedef enum {
   FLCE_K_FINALIZE = 7,    /* loss reduction                                           */
   FLCE_K_FILL = 8,        /* zero-fill / cast helpers                                 */
   FLCE_K_GATHER = 9,      /* gather of the chunk's labelled X rows (transposed)       */
-  FLCE_K_COUNT = 10
+  FLCE_K_BIAS_GRAD = 10,  /* column sums of the logit gradient into grad_bias         */
+  FLCE_K_COUNT = 11
 } flce_kernel_kind_t;
 
 typedef struct {

@@ -22,12 +22,13 @@ REDUCTIONS = {"mean": MEAN, "sum": SUM, "none": NONE}
 STATUS = {0: "FLCE_OK", -1: "FLCE_E_ARG", -2: "FLCE_E_DTYPE", -3: "FLCE_E_TARGET",
           -4: "FLCE_E_WORKSPACE", -5: "FLCE_E_HIP"}
 KERNEL_KINDS = ["mask_scan", "zero_ignored_rows", "logits_gemm", "softmax_grad", "dx_gemm",
-                "dx_reduce", "dw_gemm", "loss_finalize", "fill_cast", "gather_rows"]
+                "dx_reduce", "dw_gemm", "loss_finalize", "fill_cast", "gather_rows",
+                "bias_grad"]
 
 # Every symbol include/flce.h declares.
-EXPORTS = ["flce_chunk_size", "flce_workspace_bytes", "flce_fwd_bwd", "flce_scale_cast",
-           "flce_status_string", "flce_last_error", "flce_profile_begin", "flce_profile_end",
-           "flce_kernel_name"]
+EXPORTS = ["flce_chunk_size", "flce_workspace_bytes", "flce_fwd_bwd", "flce_workspace_bytes_ex",
+           "flce_fwd_bwd_ex", "flce_scale_cast", "flce_status_string", "flce_last_error",
+           "flce_profile_begin", "flce_profile_end", "flce_kernel_name"]
 
 
 class FlceError(RuntimeError):
@@ -49,7 +50,15 @@ class FlceStats(ctypes.Structure):
 
 
 class FlceProfile(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int64 * 10), ("total_ms", ctypes.c_double * 10)]
+    _fields_ = [("launches", ctypes.c_int64 * 11), ("total_ms", ctypes.c_double * 11)]
+
+
+class FlceOptions(ctypes.Structure):
+    """flce_options_t: the optional parts of the method (device pointers as ints)."""
+    _fields_ = [("forward_only", ctypes.c_int32), ("bias", ctypes.c_void_p),
+                ("grad_bias", ctypes.c_void_p), ("z_loss_scale", ctypes.c_float),
+                ("z_loss", ctypes.c_void_p), ("accuracy", ctypes.c_void_p),
+                ("predicted", ctypes.c_void_p)]
 
 
 _lib = None
@@ -72,6 +81,13 @@ def load():
     lib.flce_fwd_bwd.argtypes = [P, P, P, I64, I64, I64, I, I64, I, I64, I32, I, I32, I32, P, P,
                                  P, P, P, SZ, P, ctypes.POINTER(FlceStats)]
     lib.flce_fwd_bwd.restype = I
+    lib.flce_workspace_bytes_ex.argtypes = [I64, I64, I64, I, I64, I32,
+                                            ctypes.POINTER(FlceOptions)]
+    lib.flce_workspace_bytes_ex.restype = SZ
+    lib.flce_fwd_bwd_ex.argtypes = [P, P, P, I64, I64, I64, I, I64, I, I64, I32, I, I32, I32, P,
+                                    P, P, P, P, SZ, P, ctypes.POINTER(FlceStats),
+                                    ctypes.POINTER(FlceOptions)]
+    lib.flce_fwd_bwd_ex.restype = I
     lib.flce_scale_cast.argtypes = [P, I, P, I, I64, P, P]
     lib.flce_scale_cast.restype = I
     lib.flce_status_string.argtypes = [I]
@@ -108,6 +124,25 @@ def flce_fwd_bwd(X: int, W: int, targets: int, BT: int, H: int, V: int, dtype: i
                                accumulate_dw, grad_output, loss, dX, dW, workspace,
                                workspace_bytes, stream,
                                ctypes.byref(stats) if stats is not None else None)
+
+
+def flce_workspace_bytes_ex(BT: int, H: int, V: int, dtype: int, chunk_size: int = 0,
+                            chunk_mem_const: int = 1, opt: FlceOptions | None = None) -> int:
+    return load().flce_workspace_bytes_ex(BT, H, V, dtype, chunk_size, chunk_mem_const,
+                                          ctypes.byref(opt) if opt is not None else None)
+
+
+def flce_fwd_bwd_ex(X: int, W: int, targets: int, BT: int, H: int, V: int, dtype: int,
+                    ignore_index: int, reduction: int, chunk_size: int, chunk_mem_const: int,
+                    accum_dtype: int, frozen_weight: int, accumulate_dw: int, grad_output,
+                    loss: int, dX, dW, workspace: int, workspace_bytes: int, stream,
+                    stats: FlceStats | None = None, opt: FlceOptions | None = None) -> int:
+    return load().flce_fwd_bwd_ex(X, W, targets, BT, H, V, dtype, ignore_index, reduction,
+                                  chunk_size, chunk_mem_const, accum_dtype, frozen_weight,
+                                  accumulate_dw, grad_output, loss, dX, dW, workspace,
+                                  workspace_bytes, stream,
+                                  ctypes.byref(stats) if stats is not None else None,
+                                  ctypes.byref(opt) if opt is not None else None)
 
 
 def flce_scale_cast(src: int, src_dtype: int, dst: int, dst_dtype: int, n: int, scale,
@@ -160,21 +195,32 @@ class FlceResult:
     dX: "object"
     dW: "object"
     stats: dict
+    grad_bias: "object" = None
+    z_loss: "object" = None
+    accuracy: "object" = None
+    predicted: "object" = None
 
 
-def fused_linear_cross_entropy_fwd_bwd(x, weight, target, *, ignore_index: int = -100,
+def fused_linear_cross_entropy_fwd_bwd(x, weight, target, *, bias=None, ignore_index: int = -100,
                                        reduction: str = "mean", chunk_size: int | None = None,
                                        chunk_mem_const: int = 1, accum_dtype=None,
                                        frozen_weight: bool = False, grad_output=None,
-                                       dW=None, accumulate_dw: bool = False, workspace=None,
-                                       stream=None) -> FlceResult:
-    """Loss, dX and dW of fused linear cross-entropy in one call.
+                                       dW=None, accumulate_dw: bool = False,
+                                       forward_only: bool = False, z_loss_scale: float = 0.0,
+                                       return_z_loss: bool = False,
+                                       return_accuracy: bool = False,
+                                       return_predicted: bool = False, grad_bias=None,
+                                       workspace=None, stream=None) -> FlceResult:
+    """Loss, dX and dW (and optionally grad_bias and per-token outputs) in one call.
 
     x [BT, H], weight [V, H] (float32, float16 or bfloat16, on the GPU),
-    target [BT] int64.  ``accum_dtype`` None means the weight dtype; pass
-    torch.float32 for an fp32 grad_weight.  ``dW`` may be given to write into
-    (and with ``accumulate_dw`` to add to).  ``grad_output``: None, a
-    one-element float32 tensor (mean/sum) or [BT] float32 (none).
+    target [BT] int64, bias [V] (weight dtype) or None.  ``accum_dtype`` None
+    means the weight dtype; pass torch.float32 for fp32 grad_weight and
+    grad_bias.  ``dW`` / ``grad_bias`` may be given to write into (and with
+    ``accumulate_dw`` to add to).  ``grad_output``: None, a one-element
+    float32 tensor (mean/sum) or [BT] float32 (none).  ``forward_only``
+    computes the loss (and the requested per-token outputs) only.
+    ``z_loss_scale`` adds lam * lse^2 to every labelled row's loss.
     """
     import torch
     if not (x.is_cuda and weight.is_cuda and target.is_cuda):
@@ -189,34 +235,55 @@ def fused_linear_cross_entropy_fwd_bwd(x, weight, target, *, ignore_index: int =
     dt = _dtype_code(x.dtype)
     if weight.dtype != x.dtype:
         raise TypeError("x and weight must share a dtype")
+    if bias is not None:
+        if bias.dtype != x.dtype or bias.shape != (V,) or not bias.is_cuda:
+            raise TypeError("bias must be a [V] GPU tensor of the weight dtype")
+        bias = bias.contiguous()
     adt = dt if accum_dtype is None else _dtype_code(accum_dtype)
     red = REDUCTIONS[reduction]
     cs = 0 if chunk_size is None else int(chunk_size)
     dev = x.device
     loss = torch.empty(BT if red == NONE else 1, dtype=torch.float32, device=dev)
-    dX = torch.empty_like(x)
-    if not frozen_weight and dW is None:
+    nout = BT if red == NONE else 1
+    dX = None if forward_only else torch.empty_like(x)
+    if forward_only:
+        dW = None
+    elif not frozen_weight and dW is None:
         dW = torch.empty(V, H, dtype=_torch_dtype(adt), device=dev)
+    if bias is not None and not forward_only and grad_bias is None:
+        grad_bias = torch.empty(V, dtype=_torch_dtype(adt), device=dev)
+    if forward_only or bias is None:
+        grad_bias = None
+    zl = torch.empty(nout, dtype=torch.float32, device=dev) if return_z_loss else None
+    acc = torch.empty(nout, dtype=torch.float32, device=dev) if return_accuracy else None
+    pred = torch.empty(BT, dtype=torch.int64, device=dev) if return_predicted else None
+    opt = FlceOptions(int(forward_only), bias.data_ptr() if bias is not None else None,
+                      grad_bias.data_ptr() if grad_bias is not None else None,
+                      float(z_loss_scale), zl.data_ptr() if zl is not None else None,
+                      acc.data_ptr() if acc is not None else None,
+                      pred.data_ptr() if pred is not None else None)
     if grad_output is not None:
         grad_output = grad_output.to(device=dev, dtype=torch.float32).contiguous()
-    need = flce_workspace_bytes(BT, H, V, dt, cs, chunk_mem_const)
+    need = flce_workspace_bytes_ex(BT, H, V, dt, cs, chunk_mem_const, opt)
     if need == 0:
-        raise FlceError(-1, "flce_workspace_bytes")
+        raise FlceError(-1, "flce_workspace_bytes_ex")
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     st = FlceStats()
-    rc = flce_fwd_bwd(x.data_ptr(), weight.data_ptr(), target.data_ptr(), BT, H, V, dt,
-                      ignore_index, red, cs, chunk_mem_const, adt, int(frozen_weight),
-                      int(accumulate_dw), grad_output.data_ptr() if grad_output is not None
-                      else None, loss.data_ptr(), dX.data_ptr(),
-                      dW.data_ptr() if dW is not None else None, workspace.data_ptr(),
-                      workspace.numel(), stream, st)
+    rc = flce_fwd_bwd_ex(x.data_ptr(), weight.data_ptr(), target.data_ptr(), BT, H, V, dt,
+                         ignore_index, red, cs, chunk_mem_const, adt, int(frozen_weight),
+                         int(accumulate_dw), grad_output.data_ptr() if grad_output is not None
+                         else None, loss.data_ptr(), dX.data_ptr() if dX is not None else None,
+                         dW.data_ptr() if dW is not None else None, workspace.data_ptr(),
+                         workspace.numel(), stream, st, opt)
     if rc != 0:
-        raise FlceError(rc, "flce_fwd_bwd")
-    return FlceResult(loss=loss if red == NONE else loss[0], dX=dX,
-                      dW=None if frozen_weight else dW, stats=st.as_dict())
+        raise FlceError(rc, "flce_fwd_bwd_ex")
+    one = (lambda a: a) if red == NONE else (lambda a: None if a is None else a[0])
+    return FlceResult(loss=one(loss), dX=dX, dW=None if frozen_weight else dW,
+                      stats=st.as_dict(), grad_bias=grad_bias, z_loss=one(zl),
+                      accuracy=one(acc), predicted=pred)
 
 
 def scale_cast(src, dtype, scale=None, out=None):

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 #include <vector>
 
@@ -58,12 +59,28 @@ struct Layout {
   int splits = 1;
   int64_t k_per_split = 0;
   size_t off_slab = 0, off_xct = 0, off_stats = 0, off_ztgt = 0, off_partial = 0, off_idx = 0,
-         off_lossrow = 0, off_flags = 0, total = 0;
+         off_lossrow = 0, off_flags = 0, off_amax = 0, off_bias = 0, off_zrow = 0,
+         off_accrow = 0, total = 0;
 };
+
+// What the options add to a call.
+struct Extras {
+  bool forward_only = false, amax = false, bias_grad = false, zrow = false, accrow = false;
+};
+Extras extras_of(const flce_options_t* o) {
+  Extras e;
+  if (!o) return e;
+  e.forward_only = o->forward_only != 0;
+  e.amax = o->predicted || o->accuracy;
+  e.bias_grad = o->grad_bias && !e.forward_only;
+  e.zrow = o->z_loss != nullptr;
+  e.accrow = o->accuracy != nullptr;
+  return e;
+}
 
 size_t itemsize(int dt) { return dt == FLCE_F32 ? 4 : 2; }
 
-Layout make_layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t c) {
+Layout make_layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t c, const Extras& x) {
   Layout L;
   L.c = c;
   L.ldz = round_up(V, 8);
@@ -83,14 +100,20 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t c) {
     off += (size_t)round_up((int64_t)bytes, kAlign);
     return o;
   };
-  L.off_slab = take((size_t)c * L.ldz * itemsize(dtype));
-  L.off_xct = take((size_t)H * L.ldx * itemsize(dtype));
+  const bool grads = !x.forward_only;  // a loss-only call never stores logits
+  const size_t nrow = (size_t)(BT > 0 ? BT : 1);
+  L.off_slab = take(grads ? (size_t)c * L.ldz * itemsize(dtype) : 0);
+  L.off_xct = take(grads ? (size_t)H * L.ldx * itemsize(dtype) : 0);
   L.off_stats = take((size_t)c * L.stats_ld * 8);
   L.off_ztgt = take((size_t)c * 4);
-  L.off_partial = take(L.splits > 1 ? (size_t)L.splits * c * H * 4 : 0);
-  L.off_idx = take((size_t)(BT > 0 ? BT : 1) * 4);
-  L.off_lossrow = take((size_t)(BT > 0 ? BT : 1) * 4);
+  L.off_partial = take(grads && L.splits > 1 ? (size_t)L.splits * c * H * 4 : 0);
+  L.off_idx = take(nrow * 4);
+  L.off_lossrow = take(nrow * 4);
   L.off_flags = take(sizeof(ScanFlags));
+  L.off_amax = take(x.amax ? (size_t)c * L.stats_ld * 4 : 0);
+  L.off_bias = take(x.bias_grad ? (size_t)ceil_div(c, kBiasRows) * L.ldz * 4 : 0);
+  L.off_zrow = take(x.zrow ? nrow * 4 : 0);
+  L.off_accrow = take(x.accrow ? nrow * 4 : 0);
   L.total = off;
   return L;
 }
@@ -171,12 +194,18 @@ int64_t flce_chunk_size(int64_t BT, int64_t H, int64_t V, int64_t chunk_size,
   return chunk_rows(BT, H, V, chunk_size, chunk_mem_const);
 }
 
-size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,
-                            int64_t chunk_size, int32_t chunk_mem_const) {
+size_t flce_workspace_bytes_ex(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,
+                               int64_t chunk_size, int32_t chunk_mem_const,
+                               const flce_options_t* opt) {
   if (dtype < FLCE_F32 || dtype > FLCE_BF16) return 0;
   const int64_t c = chunk_rows(BT, H, V, chunk_size, chunk_mem_const);
   if (c < 1) return 0;
-  return make_layout(BT, H, V, dtype, c).total;
+  return make_layout(BT, H, V, dtype, c, extras_of(opt)).total;
+}
+
+size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,
+                            int64_t chunk_size, int32_t chunk_mem_const) {
+  return flce_workspace_bytes_ex(BT, H, V, dtype, chunk_size, chunk_mem_const, nullptr);
 }
 
 const char* flce_status_string(int status) {
@@ -196,7 +225,8 @@ const char* flce_last_error(void) { return g_last_error; }
 const char* flce_kernel_name(int kind) {
   static const char* names[FLCE_K_COUNT] = {
       "mask_scan", "zero_ignored_rows", "logits_gemm", "softmax_grad", "dx_gemm",
-      "dx_reduce", "dw_gemm",           "loss_finalize", "fill_cast",  "gather_rows"};
+      "dx_reduce", "dw_gemm",           "loss_finalize", "fill_cast",  "gather_rows",
+      "bias_grad"};
   return (kind >= 0 && kind < FLCE_K_COUNT) ? names[kind] : "unknown";
 }
 
@@ -246,12 +276,13 @@ int flce_scale_cast(const void* src, flce_dtype_t src_dtype, void* dst, flce_dty
   return FLCE_OK;
 }
 
-int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
-                 int64_t V, flce_dtype_t dtype, int64_t ignore_index, flce_reduction_t reduction,
-                 int64_t chunk_size, int32_t chunk_mem_const, flce_dtype_t accum_dtype,
-                 int32_t frozen_weight, int32_t accumulate_dw, const float* grad_output,
-                 float* loss, void* dX, void* dW, void* workspace, size_t workspace_bytes,
-                 void* stream, flce_stats_t* stats) {
+int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
+                    int64_t V, flce_dtype_t dtype, int64_t ignore_index,
+                    flce_reduction_t reduction, int64_t chunk_size, int32_t chunk_mem_const,
+                    flce_dtype_t accum_dtype, int32_t frozen_weight, int32_t accumulate_dw,
+                    const float* grad_output, float* loss, void* dX, void* dW, void* workspace,
+                    size_t workspace_bytes, void* stream, flce_stats_t* stats,
+                    const flce_options_t* opt) {
   // ---- host-side checks: nothing is launched or written on failure
   if (dtype < FLCE_F32 || dtype > FLCE_BF16) return FLCE_E_DTYPE;
   if (accum_dtype != dtype && accum_dtype != FLCE_F32) return FLCE_E_DTYPE;
@@ -262,14 +293,27 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
   if (frozen_weight != 0 && frozen_weight != 1) return FLCE_E_ARG;
   if (accumulate_dw != 0 && accumulate_dw != 1) return FLCE_E_ARG;
   if (!loss) return FLCE_E_ARG;
-  if (!frozen_weight && (!dW || !aligned(dW, 16))) return FLCE_E_ARG;
-  if (BT > 0 && (!X || !W || !targets || !dX)) return FLCE_E_ARG;
-  if (BT > 0 && (!aligned(X, 16) || !aligned(W, 16) || !aligned(dX, 16))) return FLCE_E_ARG;
+  flce_options_t o;
+  std::memset(&o, 0, sizeof o);
+  if (opt) o = *opt;
+  if (o.forward_only != 0 && o.forward_only != 1) return FLCE_E_ARG;
+  if (!(o.z_loss_scale >= 0.f) || !std::isfinite(o.z_loss_scale)) return FLCE_E_ARG;
+  if ((o.bias && !aligned(o.bias, 16)) || (o.grad_bias && !aligned(o.grad_bias, 16)) ||
+      (o.predicted && !aligned(o.predicted, 8)) || (o.z_loss && !aligned(o.z_loss, 4)) ||
+      (o.accuracy && !aligned(o.accuracy, 4)))
+    return FLCE_E_ARG;
+  const bool grads = !o.forward_only;
+  const bool want_dw = grads && !frozen_weight;
+  if (want_dw && (!dW || !aligned(dW, 16))) return FLCE_E_ARG;
+  if (BT > 0 && (!X || !W || !targets || (grads && !dX))) return FLCE_E_ARG;
+  if (BT > 0 && (!aligned(X, 16) || !aligned(W, 16) || (grads && !aligned(dX, 16))))
+    return FLCE_E_ARG;
   // The kernels address X and the logits slab with 32-bit byte offsets.
   if ((uint64_t)BT * (uint64_t)H * itemsize(dtype) > kMaxOperandBytes) return FLCE_E_ARG;
   const int64_t c = chunk_rows(BT, H, V, chunk_size, chunk_mem_const);
   if (c < 1) return FLCE_E_ARG;
-  const Layout L = make_layout(BT, H, V, dtype, c);
+  const Extras ext = extras_of(&o);
+  const Layout L = make_layout(BT, H, V, dtype, c, ext);
   if (!workspace || !aligned(workspace, kAlign)) return FLCE_E_ARG;
   if (workspace_bytes < L.total) return FLCE_E_WORKSPACE;
 
@@ -286,6 +330,11 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
   int32_t* idx = reinterpret_cast<int32_t*>(ws + L.off_idx);
   float* lossrow = reinterpret_cast<float*>(ws + L.off_lossrow);
   ScanFlags* dflags = reinterpret_cast<ScanFlags*>(ws + L.off_flags);
+  int32_t* amax = ext.amax ? reinterpret_cast<int32_t*>(ws + L.off_amax) : nullptr;
+  float* bias_partial = reinterpret_cast<float*>(ws + L.off_bias);
+  float* zrow = ext.zrow ? reinterpret_cast<float*>(ws + L.off_zrow) : nullptr;
+  float* accrow = ext.accrow ? reinterpret_cast<float*>(ws + L.off_accrow) : nullptr;
+  const bool none = reduction == FLCE_NONE;
 
   if (stats) {
     std::memset(stats, 0, sizeof *stats);
@@ -299,9 +348,14 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
   if (BT > 0) {
     FLCE_LAUNCH(FLCE_K_MASK_SCAN,
                 launch_mask_scan(targets, BT, V, ignore_index, idx, dflags, st));
-    FLCE_LAUNCH(FLCE_K_ZERO_ROWS,
-                launch_zero_ignored(targets, BT, H, ignore_index, dX, dt,
-                                    red == FLCE_NONE ? loss : nullptr, st));
+    IgnoredOut io;
+    io.dX = grads ? dX : nullptr;
+    io.dx_dtype = dt;
+    io.loss_none = none ? loss : nullptr;
+    io.z_none = none ? o.z_loss : nullptr;
+    io.acc_none = none ? o.accuracy : nullptr;
+    io.pred = o.predicted;
+    FLCE_LAUNCH(FLCE_K_ZERO_ROWS, launch_zero_ignored(targets, BT, H, ignore_index, io, st));
     if (!g_host_flags) {
       hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&g_host_flags), 64,
                                    hipHostMallocDefault);
@@ -325,8 +379,10 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
     stats->compacted = chunks < ceil_div(BT, c) ? 1 : 0;
   }
 
-  if (!frozen_weight && !accumulate_dw && chunks == 0)
+  if (want_dw && !accumulate_dw && chunks == 0)
     FLCE_LAUNCH(FLCE_K_FILL, launch_fill_zero(dW, V * H * (int64_t)itemsize(dw_dt), st));
+  if (ext.bias_grad && !accumulate_dw && chunks == 0)
+    FLCE_LAUNCH(FLCE_K_FILL, launch_fill_zero(o.grad_bias, V * (int64_t)itemsize(dw_dt), st));
 
   const float inv_n = N > 0 ? 1.0f / (float)N : 0.f;
 
@@ -334,7 +390,7 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
   int parts = (int)ceil_div(2048, c);
   const int64_t max_parts = ceil_div(L.ldz, 2048);
   if (parts > max_parts) parts = (int)max_parts;
-  if (parts < 1) parts = 1;
+  if (parts < 1 || !grads) parts = 1;
   const int64_t cols_per_part = round_up(ceil_div(L.ldz, parts), 8);
 
   // ---- the chunk loop: logits -> softmax-gradient -> dX -> dW per chunk
@@ -357,6 +413,9 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
     la.stats = stats_buf;
     la.stats_ld = L.stats_ld;
     la.ztgt = ztgt;
+    la.bias = o.bias;
+    la.amax = amax;
+    la.store_slab = grads ? 1 : 0;
     FLCE_LAUNCH(FLCE_K_LOGITS, launch_logits(dt, la, st));
 
     SoftmaxArgs sa;
@@ -376,7 +435,32 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
     sa.loss_out = loss;
     sa.parts = parts;
     sa.cols_per_part = cols_per_part;
+    sa.write_grad = grads ? 1 : 0;
+    sa.z_scale = o.z_loss_scale;
+    sa.amax = amax;
+    sa.pred_out = o.predicted;
+    sa.zrow = zrow ? zrow + base : nullptr;
+    sa.accrow = accrow ? accrow + base : nullptr;
+    sa.z_out = none ? o.z_loss : nullptr;
+    sa.acc_out = none ? o.accuracy : nullptr;
     FLCE_LAUNCH(FLCE_K_SOFTMAX, launch_softmax(dt, sa, st));
+    if (!grads) continue;
+
+    if (ext.bias_grad) {
+      BiasGradArgs ba;
+      ba.slab = slab;
+      ba.rows = rows;
+      ba.V = V;
+      ba.ldz = L.ldz;
+      ba.partial = bias_partial;
+      ba.grad_bias = o.grad_bias;
+      ba.db_dtype = dw_dt;
+      ba.accumulate = (accumulate_dw || k > 0) ? 1 : 0;
+      ba.grad_output = grad_output;
+      ba.inv_n = inv_n;
+      ba.reduction = red;
+      FLCE_LAUNCH(FLCE_K_BIAS_GRAD, launch_bias_grad(dt, ba, st));
+    }
 
     DxArgs xa;
     xa.slab = slab;
@@ -410,7 +494,7 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
       FLCE_LAUNCH(FLCE_K_DX_REDUCE, launch_dx_reduce(dt, ra, st));
     }
 
-    if (!frozen_weight) {
+    if (want_dw) {
       FLCE_LAUNCH(FLCE_K_GATHER, launch_gather_t(dt, X, cidx, rows, H, xct, L.ldx, st));
       DwArgs wa;
       wa.slab = slab;
@@ -430,9 +514,25 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
     }
   }
 
-  if (red != FLCE_NONE) FLCE_LAUNCH(FLCE_K_FINALIZE, launch_finalize(lossrow, (int)N,
-                                                                    red == FLCE_MEAN, loss, st));
+  if (!none) {
+    const int mean = red == FLCE_MEAN;
+    FLCE_LAUNCH(FLCE_K_FINALIZE, launch_finalize(lossrow, (int)N, mean, loss, st));
+    if (o.z_loss) FLCE_LAUNCH(FLCE_K_FINALIZE, launch_finalize(zrow, (int)N, mean, o.z_loss, st));
+    if (o.accuracy)
+      FLCE_LAUNCH(FLCE_K_FINALIZE, launch_finalize(accrow, (int)N, mean, o.accuracy, st));
+  }
   return FLCE_OK;
+}
+
+int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
+                 int64_t V, flce_dtype_t dtype, int64_t ignore_index, flce_reduction_t reduction,
+                 int64_t chunk_size, int32_t chunk_mem_const, flce_dtype_t accum_dtype,
+                 int32_t frozen_weight, int32_t accumulate_dw, const float* grad_output,
+                 float* loss, void* dX, void* dW, void* workspace, size_t workspace_bytes,
+                 void* stream, flce_stats_t* stats) {
+  return flce_fwd_bwd_ex(X, W, targets, BT, H, V, dtype, ignore_index, reduction, chunk_size,
+                         chunk_mem_const, accum_dtype, frozen_weight, accumulate_dw, grad_output,
+                         loss, dX, dW, workspace, workspace_bytes, stream, stats, nullptr);
 }
 
 }  // extern "C"

@@ -118,6 +118,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
   return v;
 }
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const int o = __shfl_xor(v, m, kWave);
+    v = o < v ? o : v;
+  }
+  return v;
+}
 
 // -------------------------------------------------------- XCD-aware ordering
 // Workgroups are handed to the 8 XCDs round-robin (hardware id i runs on XCD

@@ -532,6 +532,19 @@ __device__ __forceinline__ float group8_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 2, kWave));
   return fmaxf(v, __shfl_xor(v, 4, kWave));
 }
+// Maximum over 8 aligned lanes with the lowest column holding it; a lane
+// whose columns are all outside the matrix carries (-inf, INT_MAX).
+__device__ __forceinline__ void group8_argmax(float& v, int& col) {
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) {
+    const float ov = __shfl_xor(v, m, kWave);
+    const int oc = __shfl_xor(col, m, kWave);
+    if (ov > v || (ov == v && oc < col)) {
+      v = ov;
+      col = oc;
+    }
+  }
+}
 __device__ __forceinline__ float group8_sum(float v) {
   v += __shfl_xor(v, 1, kWave);
   v += __shfl_xor(v, 2, kWave);
@@ -608,10 +621,12 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
       [&](unsigned char* tile, int k0, int p) { lb.template issue<P>(wr, tile, k0, K, p); },
       (K + KT<T>::BK - 1) / KT<T>::BK, smem_raw, wm, wn, lane, acc);
 
-  // Epilogue: store the logits, and per (row, 64-column block) the max and
-  // the sum of exp(z - max) in fp32.  Both tile shapes reduce a 64-column
-  // block the same way (8 lanes x 8 values), so a row's log-sum-exp does not
-  // depend on the chunking.
+  // Epilogue: add the bias (when given; PR #1554, Tests: bias on and off),
+  // store the logits, and per (row, 64-column block) the max and the sum of
+  // exp(z - max) in fp32, plus, when predictions are wanted, the first column
+  // holding that max.  Both tile shapes reduce a 64-column block the same way
+  // (8 lanes x 8 values), so a row's log-sum-exp does not depend on the
+  // chunking.
   // The block's target columns, after the staging area (the operand stages
   // are free once the main loop is done; the epilogue's first barrier
   // publishes them).
@@ -622,23 +637,43 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   }
   S* slab = static_cast<S*>(a.slab);
   float2* stats = reinterpret_cast<float2*>(a.stats);
+  const S* bias = static_cast<const S*>(a.bias);
   staged_epilogue<C>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
                      [&](int brow, int bcol, float (&v)[8]) {
     const int gm = m0 + brow;
     const int64_t gn = n0 + bcol;
-    float mx = -INFINITY;
+    if (bias) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (gn + e < a.V) mx = fmaxf(mx, v[e]);
-    mx = group8_max(mx);
+      for (int e = 0; e < 8; ++e)
+        if (gn + e < a.V) v[e] += T::to_f32(bias[gn + e]);
+    }
+    float mx = -INFINITY;
+    int am = 0x7fffffff;  // first column of the block maximum (with a.amax)
+    if (a.amax) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gn + e < a.V && v[e] > mx) {
+          mx = v[e];
+          am = (int)(gn + e);
+        }
+      group8_argmax(mx, am);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gn + e < a.V) mx = fmaxf(mx, v[e]);
+      mx = group8_max(mx);
+    }
     float se = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (gn + e < a.V) se += __expf(v[e] - mx);
     se = group8_sum(se);
     if (gm >= a.rows || gn >= a.V) return;
-    if ((bcol & 63) == 0) stats[(int64_t)gm * a.stats_ld + gn / 64] = float2{mx, se};
-    store8<T>(slab + (int64_t)gm * a.ldz + gn, v);
+    if ((bcol & 63) == 0) {
+      stats[(int64_t)gm * a.stats_ld + gn / 64] = float2{mx, se};
+      if (a.amax) a.amax[(int64_t)gm * a.stats_ld + gn / 64] = am;
+    }
+    if (a.store_slab) store8<T>(slab + (int64_t)gm * a.ldz + gn, v);
     const int64_t tg = tgt_s[brow];
 #pragma unroll
     for (int e = 0; e < 8; ++e)

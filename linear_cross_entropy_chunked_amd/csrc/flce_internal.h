@@ -18,6 +18,9 @@ struct LogitsArgs {
   float* stats;            // [rows_cap, stats_ld] float2 (max, sum exp) per 64-column block
   int64_t stats_ld;        // in float2 units
   float* ztgt;             // [rows_cap] fp32 target logit
+  const void* bias;        // [V] operand dtype, added to every row's logits; NULL = none
+  int32_t* amax;           // [rows_cap, stats_ld] column of each block's maximum; NULL = not needed
+  int store_slab;          // 0: logits are not stored (loss-only call)
 };
 
 // Softmax-gradient pass of one chunk.
@@ -36,7 +39,30 @@ struct SoftmaxArgs {
   float* loss_out;            // none: [BT] output
   int parts;                  // workgroups per row
   int64_t cols_per_part;      // multiple of 8
+  int write_grad;             // 0: loss and per-token outputs only, the slab is not touched
+  float z_scale;              // coefficient of lse^2 in the loss (0: none)
+  const int32_t* amax;        // block argmax from the logits GEMM; NULL = no predictions
+  int64_t* pred_out;          // [BT] predicted token, or NULL
+  float* zrow;                // mean/sum: [rows] lse^2 of this chunk, or NULL
+  float* accrow;              // mean/sum: [rows] accuracy of this chunk, or NULL
+  float* z_out;               // none: [BT] lse^2 output, or NULL
+  float* acc_out;             // none: [BT] accuracy output, or NULL
 };
+// grad_bias of one chunk: column sums of G over the chunk's rows, first per
+// block of kBiasRows rows (partials), then in row-block order per column.
+struct BiasGradArgs {
+  const void* slab;  // G [rows, ldz]
+  int rows;
+  int64_t V, ldz;
+  float* partial;    // [ceil(rows_cap / kBiasRows), ldz] fp32
+  void* grad_bias;   // [V] db_dtype
+  int db_dtype;      // 0 f32, 1 f16, 2 bf16
+  int accumulate;    // 1: add to grad_bias
+  const float* grad_output;
+  float inv_n;
+  int reduction;
+};
+constexpr int kBiasRows = 32;
 
 // grad_input GEMM of one chunk.
 struct DxArgs {
@@ -94,9 +120,19 @@ hipError_t launch_mask_scan(const int64_t* targets, int64_t BT, int64_t V, int64
                             int32_t* idx, ScanFlags* flags, hipStream_t st);
 hipError_t launch_gather_t(int dtype, const void* X, const int32_t* idx, int rows, int64_t H,
                            void* XcT, int64_t ldx, hipStream_t st);
+// Outputs of an ignored row: zero dX row (dX may be NULL), and, where given,
+// zero per-token loss / z-loss / accuracy and -1 as predicted token.
+struct IgnoredOut {
+  void* dX;
+  int dx_dtype;
+  float* loss_none;
+  float* z_none;
+  float* acc_none;
+  int64_t* pred;
+};
 hipError_t launch_zero_ignored(const int64_t* targets, int64_t BT, int64_t H,
-                               int64_t ignore_index, void* dX, int dx_dtype, float* loss_none,
-                               hipStream_t st);
+                               int64_t ignore_index, const IgnoredOut& o, hipStream_t st);
+hipError_t launch_bias_grad(int dtype, const BiasGradArgs& a, hipStream_t st);
 hipError_t launch_finalize(const float* lossrow, int n, int mean, float* loss, hipStream_t st);
 hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st);
 hipError_t launch_scale_cast(const void* src, int src_dtype, void* dst, int dst_dtype,

@@ -135,24 +135,30 @@ hipError_t launch_gather_t(int dtype, const void* X, const int32_t* idx, int row
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void zero_ignored_kernel(const int64_t* __restrict__ t,
                                                            int64_t BT, int64_t row_vecs,
-                                                           int64_t ign, u32x4_t* dX,
-                                                           float* loss_none) {
+                                                           int64_t ign, IgnoredOut o) {
   for (int64_t row = blockIdx.x; row < BT; row += gridDim.x) {
     if (t[row] != ign) continue;
-    u32x4_t* p = dX + row * row_vecs;
-    for (int64_t v = threadIdx.x; v < row_vecs; v += blockDim.x) p[v] = u32x4_t{0u, 0u, 0u, 0u};
-    if (loss_none && threadIdx.x == 0) loss_none[row] = 0.f;
+    if (o.dX) {
+      u32x4_t* p = static_cast<u32x4_t*>(o.dX) + row * row_vecs;
+      for (int64_t v = threadIdx.x; v < row_vecs; v += blockDim.x)
+        p[v] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if (threadIdx.x == 0) {
+      if (o.loss_none) o.loss_none[row] = 0.f;
+      if (o.z_none) o.z_none[row] = 0.f;
+      if (o.acc_none) o.acc_none[row] = 0.f;
+      if (o.pred) o.pred[row] = -1;
+    }
   }
 }
 
 hipError_t launch_zero_ignored(const int64_t* targets, int64_t BT, int64_t H,
-                               int64_t ignore_index, void* dX, int dx_dtype, float* loss_none,
-                               hipStream_t st) {
+                               int64_t ignore_index, const IgnoredOut& o, hipStream_t st) {
   if (BT <= 0) return hipSuccess;
-  const int64_t row_bytes = H * (dx_dtype == 0 ? 4 : 2);
+  const int64_t row_bytes = H * (o.dx_dtype == 0 ? 4 : 2);
   const int grid = (int)(BT < 2048 ? BT : 2048);
   hipLaunchKernelGGL(zero_ignored_kernel, dim3(grid), dim3(256), 0, st, targets, BT,
-                     row_bytes / 16, ignore_index, static_cast<u32x4_t*>(dX), loss_none);
+                     row_bytes / 16, ignore_index, o);
   return hipGetLastError();
 }
 
@@ -162,12 +168,20 @@ hipError_t launch_zero_ignored(const int64_t* targets, int64_t BT, int64_t H,
 // the chunk:
 //   lse  = log sum_v exp(z_v), combined from the per-64-column (max, sum exp)
 //          pairs the logits GEMM left behind (fixed-order tree, fp32)
-//   loss = lse - z_t (z_t kept in fp32 by the logits GEMM)
-//   G_v  = gamma * (exp(z_v - lse) - [v == t]),  gamma = g_i for none, else 1
+//   loss = lse - z_t + lam * lse^2 (z_t kept in fp32 by the logits GEMM; lam
+//          is the optional z-loss coefficient, 0 by default)
+//   G_v  = gamma * ((1 + 2 lam lse) exp(z_v - lse) - [v == t]),
+//          gamma = g_i for none, else 1
 // written over the logits in the operand dtype (round to nearest even); the
 // slab's padding columns [V, ldz) become 0.  The mean/sum scale g/N or g is
 // applied later, in fp32, by the gradient GEMMs: folding 1/N into a 16-bit
 // slab would flush small fp16 probabilities to zero.
+// Per-token outputs (PR #1554, Details item 1 and Tests: per-token loss,
+// z-loss, accuracy and predicted token): the predicted token is the lowest
+// column holding the row maximum (the first 64-column block whose maximum is
+// the row's, then that block's first maximum, found by the logits GEMM from
+// the same fp32 values); accuracy is predicted == target; the z-loss output
+// is lse^2.
 // ---------------------------------------------------------------------------
 constexpr int SM_T = 256;
 
@@ -175,7 +189,9 @@ template <class T>
 __global__ __launch_bounds__(SM_T) void softmax_kernel(SoftmaxArgs a) {
   typedef typename T::storage S;
   __shared__ float red[SM_T / kWave];
+  __shared__ int ired[SM_T / kWave];
   __shared__ float bcast;
+  __shared__ int ibcast;
   const int m = blockIdx.x / a.parts;
   const int part = blockIdx.x % a.parts;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -194,18 +210,29 @@ __global__ __launch_bounds__(SM_T) void softmax_kernel(SoftmaxArgs a) {
   __syncthreads();
   const float M = bcast;
   float s = 0.f;
+  int first = 0x7fffffff;  // lowest block holding the row maximum
   for (int64_t j = tid; j < a.stats_n; j += SM_T) {
     const float2 p = st[j];
     s += p.y * __expf(p.x - M);
+    if (p.x == M && (int)j < first) first = (int)j;
   }
   s = wave_sum(s);
+  if (a.amax) first = wave_min_int(first);
   __syncthreads();
-  if (lane == 0) red[wave] = s;
+  if (lane == 0) {
+    red[wave] = s;
+    ired[wave] = first;
+  }
   __syncthreads();
   if (tid == 0) {
     float v = red[0];
-    for (int w = 1; w < SM_T / kWave; ++w) v += red[w];
+    int f = ired[0];
+    for (int w = 1; w < SM_T / kWave; ++w) {
+      v += red[w];
+      f = ired[w] < f ? ired[w] : f;
+    }
     bcast = v;
+    ibcast = f;
   }
   __syncthreads();
   const float lse = M + logf(bcast);
@@ -213,13 +240,25 @@ __global__ __launch_bounds__(SM_T) void softmax_kernel(SoftmaxArgs a) {
   const int64_t row = a.idx[m];
   const int64_t tgt = a.targets[row];
   if (part == 0 && tid == 0) {
-    const float l = lse - a.ztgt[m];
-    if (a.reduction == 2)
+    const float l = lse - a.ztgt[m] + a.z_scale * lse * lse;
+    const float z2 = lse * lse;
+    int64_t pred = -1;
+    if (a.amax && ibcast != 0x7fffffff) pred = a.amax[(int64_t)m * a.stats_ld + ibcast];
+    const float acc = (pred == tgt) ? 1.f : 0.f;
+    if (a.pred_out) a.pred_out[row] = pred;
+    if (a.reduction == 2) {
       a.loss_out[row] = l;
-    else
+      if (a.z_out) a.z_out[row] = z2;
+      if (a.acc_out) a.acc_out[row] = acc;
+    } else {
       a.lossrow[m] = l;
+      if (a.zrow) a.zrow[m] = z2;
+      if (a.accrow) a.accrow[m] = acc;
+    }
   }
+  if (!a.write_grad) return;
   const float gamma = (a.reduction == 2 && a.grad_output) ? a.grad_output[row] : 1.f;
+  const float pscale = gamma * (1.f + 2.f * a.z_scale * lse);
 
   S* z = static_cast<S*>(a.slab) + (int64_t)m * a.ldz;
   const int64_t c_beg = (int64_t)part * a.cols_per_part;
@@ -235,7 +274,7 @@ __global__ __launch_bounds__(SM_T) void softmax_kernel(SoftmaxArgs a) {
       float g = 0.f;
       if (col < a.V) {
         const float p = __expf(T::to_f32(e[q]) - lse);
-        g = gamma * (col == tgt ? p - 1.f : p);
+        g = col == tgt ? pscale * p - gamma : pscale * p;
       }
       e[q] = T::from_f32(g);
     }
@@ -319,6 +358,75 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const float* __restrict_
 
 hipError_t launch_finalize(const float* lossrow, int n, int mean, float* loss, hipStream_t st) {
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, st, lossrow, n, mean, loss);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// grad_bias of one chunk (PR #1554, Tests: bias on and off): the bias enters
+// every labelled row's logits, so its gradient is the column sum of G,
+// scaled like the other gradients (g/N for mean, g for sum; none carries g_i
+// inside G).  Two deterministic passes: partial sums over blocks of
+// kBiasRows rows in row order, then the blocks in order per column, added to
+// grad_bias (accumulate) or written over it.
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ __launch_bounds__(256) void bias_partial_kernel(BiasGradArgs a) {
+  typedef typename T::storage S;
+  constexpr int VE = T::vec;
+  const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * VE;
+  if (c >= a.ldz) return;
+  const int r0 = blockIdx.x * kBiasRows;
+  const int r1 = r0 + kBiasRows < a.rows ? r0 + kBiasRows : a.rows;
+  float acc[VE];
+#pragma unroll
+  for (int q = 0; q < VE; ++q) acc[q] = 0.f;
+  const S* g = static_cast<const S*>(a.slab);
+  for (int r = r0; r < r1; ++r) {
+    u32x4_t raw = *reinterpret_cast<const u32x4_t*>(g + (int64_t)r * a.ldz + c);
+    const S* e = reinterpret_cast<const S*>(&raw);
+#pragma unroll
+    for (int q = 0; q < VE; ++q) acc[q] += T::to_f32(e[q]);
+  }
+  float* out = a.partial + (int64_t)blockIdx.x * a.ldz + c;
+#pragma unroll
+  for (int q = 0; q < VE; ++q) out[q] = acc[q];
+}
+
+__global__ __launch_bounds__(256) void bias_reduce_kernel(BiasGradArgs a, int nblocks) {
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= a.V) return;
+  float s = 0.f;
+  for (int b = 0; b < nblocks; ++b) s += a.partial[(int64_t)b * a.ldz + v];
+  const float g = a.reduction == 2 ? 1.f : (a.grad_output ? a.grad_output[0] : 1.f);
+  s *= a.reduction == 0 ? g * a.inv_n : g;
+  if (a.db_dtype == 0) {
+    float* d = static_cast<float*>(a.grad_bias);
+    d[v] = a.accumulate ? d[v] + s : s;
+  } else if (a.db_dtype == 1) {
+    u16* d = static_cast<u16*>(a.grad_bias);
+    d[v] = F16::from_f32(a.accumulate ? F16::to_f32(d[v]) + s : s);
+  } else {
+    u16* d = static_cast<u16*>(a.grad_bias);
+    d[v] = BF16::from_f32(a.accumulate ? BF16::to_f32(d[v]) + s : s);
+  }
+}
+
+hipError_t launch_bias_grad(int dtype, const BiasGradArgs& a, hipStream_t st) {
+  if (a.rows <= 0) return hipSuccess;
+  const int nblocks = (a.rows + kBiasRows - 1) / kBiasRows;
+  const int ve = dtype == 0 ? 4 : 8;
+  const int64_t col_groups = (a.ldz / ve + 255) / 256;
+  const dim3 grid((unsigned)nblocks, (unsigned)col_groups);
+  if (dtype == 0)
+    hipLaunchKernelGGL(bias_partial_kernel<F32>, grid, dim3(256), 0, st, a);
+  else if (dtype == 1)
+    hipLaunchKernelGGL(bias_partial_kernel<F16>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(bias_partial_kernel<BF16>, grid, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bias_reduce_kernel, dim3((unsigned)((a.V + 255) / 256)), dim3(256), 0, st,
+                     a, nblocks);
   return hipGetLastError();
 }
 

@@ -42,7 +42,9 @@ def test_exported_symbols_in_dynamic_table(flce_lib):
 def test_status_and_kernel_names(flce_lib):
     assert flce_lib.flce_status_string(0) == "FLCE_OK"
     assert flce_lib.flce_status_string(-3).startswith("FLCE_E_TARGET")
-    assert [flce_lib.flce_kernel_name(k) for k in range(10)] == flce_lib.KERNEL_KINDS
+    n = len(flce_lib.KERNEL_KINDS)
+    assert [flce_lib.flce_kernel_name(k) for k in range(n)] == flce_lib.KERNEL_KINDS
+    assert flce_lib.flce_kernel_name(n) == "unknown"
 
 
 # ------------------------------------------------------------- chunk policy
@@ -131,3 +133,33 @@ def _call(flce_lib, **kw):
 ])
 def test_invalid_arguments_rejected_on_host(flce_lib, kw, status):
     assert _call(flce_lib, **kw) == status
+
+
+# ----------------------------------------------------------------- options
+def test_workspace_ex_follows_options(flce_lib):
+    """No options: the plain size.  Loss only: no slab.  Extras: small additions."""
+    O = flce_lib.FlceOptions
+    args = (8192, 4096, 128256, flce_lib.BF16, 2048, 1)
+    plain = flce_lib.flce_workspace_bytes(*args)
+    assert flce_lib.flce_workspace_bytes_ex(*args, None) == plain
+    assert flce_lib.flce_workspace_bytes_ex(*args, O()) == plain
+    fwd = flce_lib.flce_workspace_bytes_ex(*args, O(1))
+    assert fwd < plain - 2048 * 128256 * 2  # the [c, V] slab is gone
+    ex = flce_lib.flce_workspace_bytes_ex(*args, O(0, None, 16, 0.0, 16, 16, 16))
+    assert plain < ex < plain * 1.2
+
+
+def test_invalid_options_rejected_on_host(flce_lib):
+    """Bad options fail before any launch.  The workspace is too small on
+    purpose: a missed check would still stop at the workspace check, before
+    anything is enqueued on the fake pointers."""
+    O = flce_lib.FlceOptions
+    ws = 1
+    base = dict(X=256, W=256, targets=256, BT=4, H=8, V=16, dtype=flce_lib.F32, ignore_index=-100,
+                reduction=flce_lib.MEAN, chunk_size=4, chunk_mem_const=1, accum_dtype=flce_lib.F32,
+                frozen_weight=0, accumulate_dw=0, grad_output=None, loss=256, dX=256, dW=256,
+                workspace=256, workspace_bytes=ws, stream=None)
+    for bad in (O(2), O(0, 8), O(0, None, 8), O(0, None, None, -1.0), O(0, None, None, float("nan")),
+                O(0, None, None, 0.0, None, None, 4)):
+        rc = flce_lib.flce_fwd_bwd_ex(*base.values(), None, bad)
+        assert rc == -1, (bad.forward_only, rc)
