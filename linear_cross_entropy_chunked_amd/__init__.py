@@ -303,3 +303,4 @@ def scale_cast(src, dtype, scale=None, out=None):
 
 
 from .autograd import FusedLinearCrossEntropy, fused_linear_cross_entropy  # noqa: E402
+from .op import fused_linear_cross_entropy_op  # noqa: E402
