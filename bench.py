@@ -65,6 +65,9 @@ def parse():
     p.add_argument("--extra", default="llama3_8b_lm_head_c256",
                    help="comma-separated extra workloads reported under 'extra' ('' for none)")
     p.add_argument("--cpu-rows", type=int, default=256, help="rows in the oracle's timed sample")
+    p.add_argument("--chunk-sweep", default="",
+                   help="comma-separated chunk sizes (0: the MI355X default policy): time the "
+                        "workload at each and print one JSON line with the curve, then exit")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run plain 1 GiB device copies (reference for HBM byte counters)")
@@ -315,6 +318,32 @@ def recorded_traffic(kernel: str, workload: str):
     return float(kv["hbm_bytes_per_launch"])
 
 
+def chunk_sweep(a, cfg, dev):
+    """Time one workload at several chunk sizes (same inputs); 0 = the MI355X policy."""
+    import linear_cross_entropy_chunked_amd as pkg
+    host = None
+    rows = []
+    adt = pkg.F32 if cfg["accum"] == "f32" else {"bf16": pkg.BF16, "f16": pkg.F16,
+                                                 "f32": pkg.F32}[cfg["dtype"]]
+    dt = {"bf16": pkg.BF16, "f16": pkg.F16, "f32": pkg.F32}[cfg["dtype"]]
+    for c in [int(v) for v in a.chunk_sweep.split(",")]:
+        policy = c == 0
+        if policy:
+            c = pkg.flce_chunk_size_mi355x(cfg["BT"], cfg["H"], cfg["V"], dt, adt,
+                                           int(bool(cfg.get("frozen", False))), 0)
+        ccfg = dict(cfg, chunk=c)
+        res, host = run_workload(f"{a.workload}@{c}", ccfg, a.steps, a.warmup, dev,
+                                 None if host is None else (host, tuple(h.to(dev) for h in host)))
+        rows.append(dict(chunk=c, policy=policy, ms_per_step=res["ms_per_step"],
+                         tokens_per_s=res["tokens_per_s"], mfma_frac=res["mfma_frac"],
+                         workspace_bytes=pkg.flce_workspace_bytes(cfg["BT"], cfg["H"], cfg["V"],
+                                                                  dt, c, 1),
+                         kernels_ms_per_launch={k: round(v["ms_per_launch"], 4)
+                                                for k, v in res["kernels"].items()}))
+    print(json.dumps({"chunk_sweep": {"workload": a.workload, "steps": a.steps, "rows": rows}}),
+          flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -335,6 +364,9 @@ def main():
         log("copy calibration: 2 x 1 GiB device copies")
         copy_calibration(dev)
     cfg = WORKLOADS[a.workload]
+    if a.chunk_sweep:
+        chunk_sweep(a, cfg, dev)
+        return
     main_res, host = run_workload(a.workload, cfg, a.steps, a.warmup, dev)
     extras = {}
     for name in [e for e in a.extra.split(",") if e and e != a.workload]:

@@ -93,6 +93,35 @@ int64_t flce_chunk_size(int64_t BT, int64_t H, int64_t V, int64_t chunk_size,
                         int32_t chunk_mem_const);
 
 /*
+ * MI355X default chunk size.  The pages leave the default geometry open per
+ * GPU type (PR #1439 review thread: different defaults for GPUs with different
+ * memory, e.g. about 80 GB against about 280 GB; the heuristic's memory
+ * constant is only a proxy for the chunk size).  On MI355X (288 GB HBM3E)
+ * memory is rarely the bound, so this policy picks the smallest power of two
+ * whose per-row cost is within 10 % of the cost at an unbounded chunk, on a
+ * model of one chunk of c rows:
+ *   GEMM time  = k c' H V / (0.40 x MFMA peak)    k = 6 trained, 4 frozen;
+ *                c' = c rounded up to the 256-row tiles of the row-tiled
+ *                GEMMs (logits and grad_input; grad_weight tiles over V);
+ *                peak 2516.6 TFLOP/s for bf16/fp16, 157.3 for fp32; 0.40 is
+ *                the fraction of peak the GEMMs reach on MI355X
+ *   HBM time   = (2 V H s + 2 V H a [trained] + 5 c V s) / 5.1 TB/s
+ *                (W read by the logits and grad_input GEMMs, the dW
+ *                read-modify-write, five passes over the slab; 5.1 TB/s is
+ *                the measured device-copy rate)
+ *   chunk time = GEMM time + HBM time (the per-chunk weight traffic is not
+ *                hidden behind the GEMMs: measured per-step times fit
+ *                T(c) = T_inf + (BT / c) x 0.76 ms at BT 8192, H 4096,
+ *                V 128256)
+ * s / a: operand / accumulation item sizes.  The logits slab is kept within
+ * slab_budget_bytes (0: 2 GiB); the result is then floored to a power of two
+ * and clamped to BT like an explicit chunk_size.  Returns >= 1, or FLCE_E_ARG.
+ */
+int64_t flce_chunk_size_mi355x(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,
+                               flce_dtype_t accum_dtype, int32_t frozen_weight,
+                               size_t slab_budget_bytes);
+
+/*
  * Bytes of device workspace flce_fwd_bwd needs for these arguments.  The
  * dominant term is the [chunk_size, V] logits slab in the operand dtype
  * (chunk_size x V x itemsize, PR #1439, Summary), so with an explicit

@@ -26,7 +26,7 @@ KERNEL_KINDS = ["mask_scan", "zero_ignored_rows", "logits_gemm", "softmax_grad",
                 "bias_grad"]
 
 # Every symbol include/flce.h declares.
-EXPORTS = ["flce_chunk_size", "flce_workspace_bytes", "flce_fwd_bwd", "flce_workspace_bytes_ex",
+EXPORTS = ["flce_chunk_size", "flce_chunk_size_mi355x", "flce_workspace_bytes", "flce_fwd_bwd", "flce_workspace_bytes_ex",
            "flce_fwd_bwd_ex", "flce_scale_cast", "flce_status_string", "flce_last_error",
            "flce_profile_begin", "flce_profile_end", "flce_kernel_name"]
 
@@ -76,6 +76,8 @@ def load():
     I = ctypes.c_int
     lib.flce_chunk_size.argtypes = [I64, I64, I64, I64, I32]
     lib.flce_chunk_size.restype = I64
+    lib.flce_chunk_size_mi355x.argtypes = [I64, I64, I64, I, I, I32, SZ]
+    lib.flce_chunk_size_mi355x.restype = I64
     lib.flce_workspace_bytes.argtypes = [I64, I64, I64, I, I64, I32]
     lib.flce_workspace_bytes.restype = SZ
     lib.flce_fwd_bwd.argtypes = [P, P, P, I64, I64, I64, I, I64, I, I64, I32, I, I32, I32, P, P,
@@ -107,6 +109,12 @@ def load():
 # ----------------------------------------------------------- C-ABI mirrors
 def flce_chunk_size(BT: int, H: int, V: int, chunk_size: int = 0, chunk_mem_const: int = 1) -> int:
     return load().flce_chunk_size(BT, H, V, chunk_size, chunk_mem_const)
+
+
+def flce_chunk_size_mi355x(BT: int, H: int, V: int, dtype: int, accum_dtype: int,
+                           frozen_weight: int = 0, slab_budget_bytes: int = 0) -> int:
+    return load().flce_chunk_size_mi355x(BT, H, V, dtype, accum_dtype, frozen_weight,
+                                         slab_budget_bytes)
 
 
 def flce_workspace_bytes(BT: int, H: int, V: int, dtype: int, chunk_size: int = 0,
@@ -218,7 +226,9 @@ def fused_linear_cross_entropy_fwd_bwd(x, weight, target, *, bias=None, ignore_i
     means the weight dtype; pass torch.float32 for fp32 grad_weight and
     grad_bias.  ``dW`` / ``grad_bias`` may be given to write into (and with
     ``accumulate_dw`` to add to).  ``grad_output``: None, a one-element
-    float32 tensor (mean/sum) or [BT] float32 (none).  ``forward_only``
+    float32 tensor (mean/sum) or [BT] float32 (none).  ``chunk_size``: None
+    for the pages' heuristic, an int (floored to a power of two, clamped to
+    BT), or "mi355x" (or -1) for the MI355X policy.  ``forward_only``
     computes the loss (and the requested per-token outputs) only.
     ``z_loss_scale`` adds lam * lse^2 to every labelled row's loss.
     """
@@ -241,7 +251,14 @@ def fused_linear_cross_entropy_fwd_bwd(x, weight, target, *, bias=None, ignore_i
         bias = bias.contiguous()
     adt = dt if accum_dtype is None else _dtype_code(accum_dtype)
     red = REDUCTIONS[reduction]
-    cs = 0 if chunk_size is None else int(chunk_size)
+    if chunk_size in ("mi355x", -1):  # the MI355X default policy
+        c = flce_chunk_size_mi355x(BT, H, V, dt, adt, int(bool(frozen_weight)), 0)
+        # c is a power of two, or BT when one chunk covers every row; as an
+        # explicit size (floored to a power of two, then clamped to BT) its
+        # next power of two gives exactly c rows
+        cs = 1 << max(int(c) - 1, 0).bit_length() if c > 0 else 0
+    else:
+        cs = 0 if chunk_size is None else int(chunk_size)
     dev = x.device
     loss = torch.empty(BT if red == NONE else 1, dtype=torch.float32, device=dev)
     nout = BT if red == NONE else 1

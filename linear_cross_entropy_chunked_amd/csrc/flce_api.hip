@@ -54,6 +54,15 @@ constexpr int kDxTargetBlocks = 256;     // one workgroup per CU on 256 CUs
 constexpr int64_t kDxMinKPerSplit = 1024;
 constexpr int kDxMaxSplits = 32;
 
+// MI355X chunk policy model (see flce_chunk_size_mi355x in flce.h).
+constexpr double kMfma16 = 2516.6e12;           // dense bf16/fp16 MFMA peak, FLOP/s
+constexpr double kMfmaF32 = 157.3e12;           // dense fp32 MFMA peak, FLOP/s
+constexpr double kGemmEfficiency = 0.40;        // measured fraction of peak of the GEMMs
+constexpr double kHbmBytesPerSecond = 5.1e12;   // measured device-copy rate
+constexpr double kSlabPasses = 5.0;             // slab: write, read+write, read by dX and dW
+constexpr double kPolicyTolerance = 1.10;       // accept 10 % above the large-chunk cost
+constexpr size_t kDefaultSlabBudget = 2ull << 30;  // 2 GiB logits slab
+
 struct Layout {
   int64_t c = 0, ldz = 0, ldx = 0, stats_ld = 0;
   int splits = 1;
@@ -192,6 +201,37 @@ extern "C" {
 int64_t flce_chunk_size(int64_t BT, int64_t H, int64_t V, int64_t chunk_size,
                         int32_t chunk_mem_const) {
   return chunk_rows(BT, H, V, chunk_size, chunk_mem_const);
+}
+
+int64_t flce_chunk_size_mi355x(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,
+                               flce_dtype_t accum_dtype, int32_t frozen_weight,
+                               size_t slab_budget_bytes) {
+  if (BT < 0 || H < 1 || V < 1) return FLCE_E_ARG;
+  if (dtype < FLCE_F32 || dtype > FLCE_BF16) return FLCE_E_ARG;
+  if (accum_dtype != dtype && accum_dtype != FLCE_F32) return FLCE_E_ARG;
+  if (BT == 0) return 1;
+  const double s = (double)itemsize(dtype), a = (double)itemsize(accum_dtype);
+  const double Hd = (double)H, Vd = (double)V;
+  const double rate = (dtype == FLCE_F32 ? kMfmaF32 : kMfma16) * kGemmEfficiency;
+  const double k = frozen_weight ? 4.0 : 6.0;
+  // Time of one chunk of c rows: the larger of its GEMM time and its HBM time.
+  auto chunk_time = [&](double c) {
+    // the row-tiled GEMMs (logits, grad_input) compute whole 256-row tiles
+    const double c_tiles = std::ceil(c / 256.0) * 256.0;
+    const double flops = (k - 2.0) * c_tiles * Hd * Vd + 2.0 * c * Hd * Vd;
+    double bytes = 2.0 * Vd * Hd * s + kSlabPasses * c * Vd * s;
+    if (!frozen_weight) bytes += 2.0 * a * Vd * Hd;
+    return flops / rate + bytes / kHbmBytesPerSecond;
+  };
+  // Per-row cost as c grows without bound.
+  const double floor_row = k * Hd * Vd / rate + kSlabPasses * Vd * s / kHbmBytesPerSecond;
+  const size_t budget = slab_budget_bytes ? slab_budget_bytes : kDefaultSlabBudget;
+  int64_t cap = (int64_t)(budget / (size_t)((double)V * s));
+  if (cap < 1) cap = 1;
+  int64_t c = 1;
+  while (c * 2 <= cap && c < BT && chunk_time((double)c) / (double)c > kPolicyTolerance * floor_row)
+    c *= 2;
+  return chunk_rows(BT, H, V, c, 1);
 }
 
 size_t flce_workspace_bytes_ex(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,

@@ -163,3 +163,45 @@ def test_invalid_options_rejected_on_host(flce_lib):
                 O(0, None, None, 0.0, None, None, 4)):
         rc = flce_lib.flce_fwd_bwd_ex(*base.values(), None, bad)
         assert rc == -1, (bad.forward_only, rc)
+
+
+# ------------------------------------------------------ MI355X chunk policy
+POLICY_SHAPES = [  # BT, H, V, dtype, accum, frozen
+    (8192, 4096, 128256, 2, 0, 0), (16384, 4096, 32000, 2, 2, 0), (16384, 4096, 32000, 0, 0, 0),
+    (8192, 5376, 262144, 2, 2, 0), (32768, 5376, 262144, 2, 2, 0), (8192, 2048, 151936, 2, 2, 1),
+    (256, 128, 1024, 0, 0, 0), (100, 64, 50, 1, 0, 0)]
+
+
+@pytest.mark.parametrize("shape", POLICY_SHAPES)
+def test_policy_is_a_clamped_power_of_two_within_budget(flce_lib, shape):
+    BT, H, V, dt, adt, fr = shape
+    s = 4 if dt == 0 else 2
+    for budget in (0, 1 << 28, 1 << 33):
+        c = flce_lib.flce_chunk_size_mi355x(BT, H, V, dt, adt, fr, budget)
+        assert 1 <= c <= BT
+        assert c == BT or (c & (c - 1)) == 0
+        assert c == 1 or c * V * s <= (budget or (2 << 30))
+
+
+def test_policy_monotone_in_budget_and_work(flce_lib):
+    f = flce_lib.flce_chunk_size_mi355x
+    cs = [f(8192, 4096, 128256, 2, 0, 0, b) for b in (1 << 24, 1 << 26, 1 << 28, 1 << 30, 0)]
+    assert cs == sorted(cs)
+    # freezing the weight removes the dW traffic, so a smaller chunk suffices
+    assert f(8192, 2048, 151936, 2, 2, 1, 0) <= f(8192, 2048, 151936, 2, 2, 0, 0)
+
+
+def test_policy_choices_at_benchmark_shapes(flce_lib):
+    """The model's choices (validated by bench.py --chunk-sweep on MI355X)."""
+    f = flce_lib.flce_chunk_size_mi355x
+    assert f(8192, 4096, 128256, 2, 0, 0, 0) == 4096
+    assert f(8192, 4096, 128256, 2, 0, 0, 1 << 28) == 1024  # 256 MiB slab budget
+    assert f(16384, 4096, 32000, 2, 2, 0, 0) == 4096
+
+
+def test_policy_rejects_invalid_arguments(flce_lib):
+    f = flce_lib.flce_chunk_size_mi355x
+    assert f(-1, 8, 8, 2, 2, 0, 0) == -1
+    assert f(8, 0, 8, 2, 2, 0, 0) == -1
+    assert f(8, 8, 8, 7, 7, 0, 0) == -1
+    assert f(8, 8, 8, 2, 1, 0, 0) == -1  # bf16 operands with an fp16 accumulator

@@ -197,3 +197,18 @@ def test_all_rows_ignored_with_options(pkg):
     assert float(r.loss) == 0.0 and float(r.z_loss) == 0.0 and float(r.accuracy) == 0.0
     assert torch.all(r.predicted == -1)
     assert torch.all(r.grad_bias == 0) and torch.all(r.dW == 0) and torch.all(r.dX == 0)
+
+
+def test_mi355x_policy_is_an_explicit_chunk(pkg):
+    """chunk_size="mi355x" runs exactly as the chunk size the policy returns."""
+    BT, H, V = 640, 64, 500
+    X, W, t, _ = _case(BT, H, V, "bf16", seed=12)
+    dev = torch.device("cuda:0")
+    args = (X.to(dev), W.to(dev), t.to(dev))
+    c = pkg.flce_chunk_size_mi355x(BT, H, V, pkg.BF16, pkg.F32, 0, 0)
+    a = pkg.fused_linear_cross_entropy_fwd_bwd(*args, chunk_size="mi355x",
+                                               accum_dtype=torch.float32)
+    b = pkg.fused_linear_cross_entropy_fwd_bwd(*args, chunk_size=c, accum_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert a.stats["chunk_size"] == c
+    assert torch.equal(a.loss, b.loss) and torch.equal(a.dX, b.dX) and torch.equal(a.dW, b.dW)
