@@ -140,12 +140,12 @@ struct RowSwz {
   // LDS serves 256 bytes per cycle (64 banks): the 16 rows read by 16
   // consecutive lanes must land in 16 distinct 16-byte slots of that window.
   // 128-byte rows: chunk ^= (r / 2) % 8; 64-byte rows: chunk ^= (r / 4) % 4.
-  __device__ static int swz(int r) { return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
-  __device__ static u32x4_t frag16(const unsigned char* b, int r, int s, int lane) {
+  __device__ __forceinline__ static int swz(int r) { return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+  __device__ __forceinline__ static u32x4_t frag16(const unsigned char* b, int r, int s, int lane) {
     const int kc = 2 * s + (lane >> 5);
     return *reinterpret_cast<const u32x4_t*>(b + r * RB + ((kc ^ swz(r)) << 4));
   }
-  __device__ static float frag4(const unsigned char* b, int r, int k) {
+  __device__ __forceinline__ static float frag4(const unsigned char* b, int r, int k) {
     return reinterpret_cast<const float*>(b + r * RB + (((k >> 2) ^ swz(r)) << 4))[k & 3];
   }
 };
@@ -159,12 +159,12 @@ struct ColSwz {
   // 16-bit: the 4 k-rows of one transposing read move by 64 bytes each
   // (chunk ^= 4 (k % 4)); fp32: odd k-rows move by 128 bytes (chunk ^= 8 (k % 2)).
   static_assert(RBT >= 256, "column swizzle needs 16 chunks per k-row");
-  __device__ static int swz(int k) { return sizeof(S) == 2 ? 4 * (k & 3) : 8 * (k & 1); }
-  __device__ static const unsigned char* at(const unsigned char* b, int k, int c) {
+  __device__ __forceinline__ static int swz(int k) { return sizeof(S) == 2 ? 4 * (k & 3) : 8 * (k & 1); }
+  __device__ __forceinline__ static const unsigned char* at(const unsigned char* b, int k, int c) {
     return b + k * RBT + (((c / EPC) ^ swz(k)) << 4) + (c % EPC) * (int)sizeof(S);
   }
   // c: first column of the 32-column MFMA block
-  __device__ static u32x4_t frag16(const unsigned char* b, int c, int s, int lane) {
+  __device__ __forceinline__ static u32x4_t frag16(const unsigned char* b, int c, int s, int lane) {
     const int q = lane & 15;
     const int col = c + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
     const int k1 = 16 * s + 8 * (lane >> 5) + (q >> 2);
@@ -175,7 +175,7 @@ struct ColSwz {
     const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
     return u32x4_t{l2[0], l2[1], h2[0], h2[1]};
   }
-  __device__ static float frag4(const unsigned char* b, int c, int k) {
+  __device__ __forceinline__ static float frag4(const unsigned char* b, int c, int k) {
     return *reinterpret_cast<const float*>(at(b, k, c));
   }
 };
@@ -205,7 +205,7 @@ struct DmaRows {
   int wave;
 
   template <class RowFn>
-  __device__ void init(int tid, RowFn rowoff) {
+  __device__ __forceinline__ void init(int tid, RowFn rowoff) {
     const int lane = tid & 63;
     wave = tid >> 6;
     const int rin = lane / CPR;
@@ -219,7 +219,7 @@ struct DmaRows {
   // Part `part` of P: the instructions i with i * P / NI == part (P parts
   // spread the tile's loads over the P k-steps of the previous tile).
   template <int P>
-  __device__ void issue(desc_t rs, unsigned char* tile, int k0, int kend,
+  __device__ __forceinline__ void issue(desc_t rs, unsigned char* tile, int k0, int kend,
                         int part) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -254,7 +254,7 @@ struct DmaCols {
   uint32_t cofs[NI]; // byte offset of this lane's column chunk (kOOB: outside)
   int wave;
 
-  __device__ void init(int tid, int c0, int cend) {
+  __device__ __forceinline__ void init(int tid, int c0, int cend) {
     const int lane = tid & 63;
     wave = tid >> 6;
     const int rin = lane / CPRT, p = lane % CPRT;
@@ -266,7 +266,7 @@ struct DmaCols {
     }
   }
   template <int P, class KFn>
-  __device__ void issue(desc_t rs, unsigned char* tile, int k0, KFn rowoff,
+  __device__ __forceinline__ void issue(desc_t rs, unsigned char* tile, int k0, KFn rowoff,
                         int part) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -318,7 +318,7 @@ __device__ __forceinline__ float frag4_of(const unsigned char* b, int blk, int s
 // MFMAs (mask 0x008), read q followed by its share of MFMAs.
 template <int NR, int NM, int Q = 0>
 struct PinInterleave {
-  __device__ static void run() {
+  __device__ __forceinline__ static void run() {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     constexpr int m = (NM * (Q + 1)) / NR - (NM * Q) / NR;
     if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
@@ -327,7 +327,7 @@ struct PinInterleave {
 };
 template <int NR, int NM>
 struct PinInterleave<NR, NM, NR> {
-  __device__ static void run() {}
+  __device__ __forceinline__ static void run() {}
 };
 
 template <class T, class C, class LA, class LB, class DMA>
@@ -488,7 +488,12 @@ __device__ __forceinline__ void staged_epilogue(float* stage, const f32x16_t (&a
           }
     }
     __syncthreads();
-    for (int q = tid; q < C::WTM * SUBS; q += C::NT) {
+    // Fully unrolled, so that the pieces' cross-lane reductions and stores
+    // overlap instead of running as one dependent chain per piece.
+    constexpr int NQ = C::WTM * SUBS / C::NT;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int q = tid + i * C::NT;
       const int lrow = q / SUBS, piece = q % SUBS;
       const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8);
       const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8 + 4);
@@ -527,28 +532,45 @@ __device__ __forceinline__ void store8(typename T::storage* p, const float (&v)[
   }
 }
 
+// Reductions over 8 aligned lanes with DPP moves (no LDS traffic): swap
+// neighbours (quad_perm [1,0,3,2]), swap pairs (quad_perm [2,3,0,1]), then
+// mirror within each half-row of 8 lanes (row_half_mirror), which pairs
+// every lane of one quad with a lane of the other.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppSwap1 = 0xb1, kDppSwap2 = 0x4e, kDppHalfMirror = 0x141;
+
 __device__ __forceinline__ float group8_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1, kWave));
-  v = fmaxf(v, __shfl_xor(v, 2, kWave));
-  return fmaxf(v, __shfl_xor(v, 4, kWave));
+  v = fmaxf(v, dpp_f<kDppSwap1>(v));
+  v = fmaxf(v, dpp_f<kDppSwap2>(v));
+  return fmaxf(v, dpp_f<kDppHalfMirror>(v));
 }
 // Maximum over 8 aligned lanes with the lowest column holding it; a lane
 // whose columns are all outside the matrix carries (-inf, INT_MAX).
-__device__ __forceinline__ void group8_argmax(float& v, int& col) {
-#pragma unroll
-  for (int m = 1; m < 8; m <<= 1) {
-    const float ov = __shfl_xor(v, m, kWave);
-    const int oc = __shfl_xor(col, m, kWave);
-    if (ov > v || (ov == v && oc < col)) {
-      v = ov;
-      col = oc;
-    }
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& col) {
+  const float ov = dpp_f<CTRL>(v);
+  const int oc = dpp_i<CTRL>(col);
+  if (ov > v || (ov == v && oc < col)) {
+    v = ov;
+    col = oc;
   }
 }
+__device__ __forceinline__ void group8_argmax(float& v, int& col) {
+  argmax_step<kDppSwap1>(v, col);
+  argmax_step<kDppSwap2>(v, col);
+  argmax_step<kDppHalfMirror>(v, col);
+}
 __device__ __forceinline__ float group8_sum(float v) {
-  v += __shfl_xor(v, 1, kWave);
-  v += __shfl_xor(v, 2, kWave);
-  return v + __shfl_xor(v, 4, kWave);
+  v += dpp_f<kDppSwap1>(v);
+  v += dpp_f<kDppSwap2>(v);
+  return v + dpp_f<kDppHalfMirror>(v);
 }
 
 // Upstream scale s for mean / sum (grad_output may be NULL = 1).
@@ -639,7 +661,7 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   float2* stats = reinterpret_cast<float2*>(a.stats);
   const S* bias = static_cast<const S*>(a.bias);
   staged_epilogue<C>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
-                     [&](int brow, int bcol, float (&v)[8]) {
+                     [&](int brow, int bcol, float (&v)[8]) __attribute__((always_inline)) {
     const int gm = m0 + brow;
     const int64_t gn = n0 + bcol;
     if (bias) {
@@ -748,7 +770,7 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
   float* part = a.partial + (int64_t)split * a.rows_cap * H;
   const bool direct = a.splits == 1;
   staged_epilogue<C>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
-                     [&](int brow, int bcol, float (&v)[8]) {
+                     [&](int brow, int bcol, float (&v)[8]) __attribute__((always_inline)) {
     const int gm = m0 + brow;
     const int gn = n0 + bcol;
     if (gm >= a.rows || gn >= H) return;
