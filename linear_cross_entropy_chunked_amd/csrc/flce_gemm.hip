@@ -662,44 +662,66 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   const S* bias = static_cast<const S*>(a.bias);
   staged_epilogue<C>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
                      [&](int brow, int bcol, float (&v)[8]) __attribute__((always_inline)) {
+    // Branch-free except where a piece straddles the end of the vocabulary:
+    // columns past V are masked to -inf for the statistics by selects.
     const int gm = m0 + brow;
     const int64_t gn = n0 + bcol;
+    const int64_t left = a.V - gn;
+    const int nv = left >= 8 ? 8 : (left > 0 ? (int)left : 0);  // valid columns here
     if (bias) {
+      if (nv == 8) {
+        float b8[8];
+        if constexpr (sizeof(S) == 2) {
+          unpack8<T>(*reinterpret_cast<const u32x4_t*>(bias + gn), b8);
+        } else {
+          const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(bias + gn);
+          const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(bias + gn + 4);
+          b8[0] = lo[0], b8[1] = lo[1], b8[2] = lo[2], b8[3] = lo[3];
+          b8[4] = hi[0], b8[5] = hi[1], b8[6] = hi[2], b8[7] = hi[3];
+        }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (gn + e < a.V) v[e] += T::to_f32(bias[gn + e]);
+        for (int e = 0; e < 8; ++e) v[e] += b8[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e < nv) v[e] += T::to_f32(bias[gn + e]);
+      }
     }
+    float w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = e < nv ? v[e] : -INFINITY;
     float mx = -INFINITY;
     int am = 0x7fffffff;  // first column of the block maximum (with a.amax)
     if (a.amax) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (gn + e < a.V && v[e] > mx) {
-          mx = v[e];
-          am = (int)(gn + e);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const bool gt = w[e] > mx;
+        am = gt ? (int)(gn + e) : am;
+        mx = gt ? w[e] : mx;
+      }
       group8_argmax(mx, am);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (gn + e < a.V) mx = fmaxf(mx, v[e]);
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, w[e]);
       mx = group8_max(mx);
     }
+    // exp(-inf - mx) = 0 for masked columns; a group whose 64 columns all lie
+    // past V gets NaN here but is never stored.
     float se = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (gn + e < a.V) se += __expf(v[e] - mx);
+    for (int e = 0; e < 8; ++e) se += __expf(w[e] - mx);
     se = group8_sum(se);
-    if (gm >= a.rows || gn >= a.V) return;
+    if (gm >= a.rows || nv == 0) return;
     if ((bcol & 63) == 0) {
       stats[(int64_t)gm * a.stats_ld + gn / 64] = float2{mx, se};
       if (a.amax) a.amax[(int64_t)gm * a.stats_ld + gn / 64] = am;
     }
     if (a.store_slab) store8<T>(slab + (int64_t)gm * a.ldz + gn, v);
-    const int64_t tg = tgt_s[brow];
+    const int64_t d = tgt_s[brow] - gn;  // target column within this piece, if any
+    float zt = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (gn + e == tg) a.ztgt[gm] = v[e];
+    for (int e = 0; e < 8; ++e) zt = d == e ? v[e] : zt;
+    if (d >= 0 && d < 8) a.ztgt[gm] = zt;
   });
 }
 
@@ -969,7 +991,7 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t st) {
 // read-modify-write, where two resident workgroups per CU hide more latency.
 bool logits_big(int rows, int64_t V) { return rows > 128 && V >= 1024; }
 bool dx_big(int rows, int64_t H) { return rows > 128 && H >= 256; }
-bool dw_big(int rows, int64_t H) { return rows > 512 && H >= 256; }
+bool dw_big(int rows, int64_t H) { return rows > 256 && H >= 256; }
 
 template <class T>
 static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
