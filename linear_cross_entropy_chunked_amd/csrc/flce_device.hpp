@@ -20,12 +20,16 @@ constexpr int kWave = 64;
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_to_f32(u16 b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// fp32 -> bf16, IEEE round-to-nearest-even; NaN stays NaN.
+// fp32 -> bf16, IEEE round-to-nearest-even (gfx950's v_cvt_pk_bf16_f32);
+// NaN stays NaN.  The pair form converts two values in one instruction.
+typedef __bf16 bf16x2_native_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_native_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  const f32x2_native_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_native_t));
+}
 __device__ __forceinline__ u16 f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return u16((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u16(u >> 16);
+  return __builtin_bit_cast(u16, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ float f16_to_f32(u16 h) {

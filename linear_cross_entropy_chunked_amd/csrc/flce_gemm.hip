@@ -508,8 +508,12 @@ template <class T>
 __device__ __forceinline__ u32x4_t pack8(const float (&v)[8]) {
   u32x4_t o;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    o[e] = (uint32_t)T::from_f32(v[2 * e]) | ((uint32_t)T::from_f32(v[2 * e + 1]) << 16);
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (std::is_same<T, BF16>::value)
+      o[e] = f32x2_to_bf16x2(v[2 * e], v[2 * e + 1]);
+    else
+      o[e] = (uint32_t)T::from_f32(v[2 * e]) | ((uint32_t)T::from_f32(v[2 * e + 1]) << 16);
+  }
   return o;
 }
 template <class T>
