@@ -45,12 +45,12 @@ constexpr int kKBytes = 128;
 // LDS stages per operand (2 or 3; at most one operand with 3), per kernel.
 // A tile is needed S - 1 iterations after its loads are issued, so a third
 // stage doubles the time that operand's loads have to arrive.
-constexpr int kLogitsStagesA = 2, kLogitsStagesB = 2;
-constexpr int kDxStagesA = 2, kDxStagesB = 2;
-constexpr int kDwStagesA = 2, kDwStagesB = 2;
+constexpr int kLogitsStagesA = 3, kLogitsStagesB = 2;
+constexpr int kDxStagesA = 3, kDxStagesB = 2;
+constexpr int kDwStagesA = 2, kDwStagesB = 3;
 // Parts each k-tile's loads are split into, spread over the k-steps of the
 // previous tile's MFMA work (1: all issued after the first k-step).
-constexpr int kLogitsParts = 1, kDxParts = 2, kDwParts = 4;
+constexpr int kLogitsParts = 2, kDxParts = 2, kDwParts = 4;
 
 template <class T>
 struct KT {
@@ -409,10 +409,16 @@ __device__ __forceinline__ void main_loop(IA ia, IB ib, int nk, unsigned char* s
   constexpr int LA = SA - 1, LB = SB - 1;
   constexpr int LEAD = LA > LB ? LA : LB;
   constexpr int PER_IT = OA::NI + OB::NI;
-  // loads issued after the later of A's and B's tile t
+  // Loads issued after the later of A's and B's tile t.  Each iteration
+  // issues its loads in P parts, each part the near operand's share and then
+  // the far operand's, so after the near operand's last part only the far
+  // operand's last part follows within that iteration.
+  // instructions in part P - 1: i with i * P / NI == P - 1, i.e. i >= ceil((P - 1) NI / P)
+  constexpr int LAST_A = OA::NI - ((P - 1) * OA::NI + P - 1) / P;
+  constexpr int LAST_B = OB::NI - ((P - 1) * OB::NI + P - 1) / P;
   constexpr int AFTER = LA == LB ? (LA - 1) * PER_IT
-                        : LA > LB ? OA::NI + (LB - 1) * PER_IT
-                                  : OB::NI + (LA - 1) * PER_IT;
+                        : LA > LB ? LAST_A + (LB - 1) * PER_IT
+                                  : LAST_B + (LA - 1) * PER_IT;
   static_assert(AFTER < 64, "vmcnt range");
   auto tile_a = [&](int j) { return smem + (j % SA) * OA::TILE_BYTES; };
   auto tile_b = [&](int j) { return smem + SM::B_OFS + (j % SB) * OB::TILE_BYTES; };
