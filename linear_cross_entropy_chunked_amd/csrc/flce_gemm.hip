@@ -45,7 +45,7 @@ constexpr int kKBytes = 128;
 // LDS stages per operand (2 or 3; at most one operand with 3), per kernel.
 // A tile is needed S - 1 iterations after its loads are issued, so a third
 // stage doubles the time that operand's loads have to arrive.
-constexpr int kLogitsStagesA = 3, kLogitsStagesB = 2;
+constexpr int kLogitsStagesA = 2, kLogitsStagesB = 3;
 constexpr int kDxStagesA = 3, kDxStagesB = 2;
 constexpr int kDwStagesA = 2, kDwStagesB = 3;
 // Parts each k-tile's loads are split into, spread over the k-steps of the
