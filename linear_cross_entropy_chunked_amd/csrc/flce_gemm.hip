@@ -12,8 +12,9 @@
 // rows of m/n, both with an XOR swizzle of their 16-byte chunks.  MFMA
 // fragments are read with 16-byte LDS reads (k-contiguous tiles) or with two
 // transposing 8-byte reads (m/n-contiguous tiles); the swizzles keep both
-// kinds free of bank conflicts on gfx950's 64-bank LDS.  Two LDS stages: the
-// next k-tile streams in while the current one is multiplied.
+// kinds free of bank conflicts on gfx950's 64-bank LDS.  Two or three LDS
+// stages per operand: later k-tiles stream in while the current one is
+// multiplied, their loads spread over its MFMA k-steps.
 //
 // Two tile shapes: 256x256 blocks of four 128x128 waves (one workgroup per
 // CU) for the compute-bound shapes, and 128x128 blocks of four 64x64 waves
@@ -42,9 +43,9 @@ typedef Cfg<128, 128> Small;
 // beat 64-byte rows, whose extra barriers cost more than their extra stages
 // gain.)
 constexpr int kKBytes = 128;
-// LDS stages per operand (2 or 3; at most one operand with 3), per kernel.
-// A tile is needed S - 1 iterations after its loads are issued, so a third
-// stage doubles the time that operand's loads have to arrive.
+// LDS stages per operand, per kernel (measured on MI355X).  A tile is needed
+// S - 1 iterations after its loads are issued, so a third stage doubles the
+// time that operand's loads have to arrive.
 constexpr int kLogitsStagesA = 2, kLogitsStagesB = 3;
 constexpr int kDxStagesA = 3, kDxStagesB = 2;
 constexpr int kDwStagesA = 2, kDwStagesB = 3;
@@ -188,9 +189,9 @@ struct ColSwz {
 // k-contiguous source into a RowSwz tile.  Tile row r starts at byte offset
 // rowoff(r) (kOOB: zero row) of the descriptor.  An instruction fills RPI =
 // 1024 / RB rows: lane L takes row L / CPR of its group and physical chunk
-// L % CPR, i.e. k-chunk (L % CPR) ^ swz(row).  Chunks whose first k is >= kend read as zero;
-// callers keep kend a multiple of the chunk width, and elements between the
-// logical K and kend are zero in memory.
+// L % CPR, i.e. k-chunk (L % CPR) ^ swz(row).  Chunks whose first k is >=
+// kend read as zero; callers keep kend a multiple of the chunk width, and
+// elements between the logical K and kend are zero in memory.
 template <class T, int R, int NWAVES>
 struct DmaRows {
   typedef RowSwz<T> Layout;
@@ -220,7 +221,7 @@ struct DmaRows {
   // spread the tile's loads over the P k-steps of the previous tile).
   template <int P>
   __device__ __forceinline__ void issue(desc_t rs, unsigned char* tile, int k0, int kend,
-                        int part) const {
+                                        int part) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if (i * P / NI != part) continue;
@@ -267,7 +268,7 @@ struct DmaCols {
   }
   template <int P, class KFn>
   __device__ __forceinline__ void issue(desc_t rs, unsigned char* tile, int k0, KFn rowoff,
-                        int part) const {
+                                        int part) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if (i * P / NI != part) continue;
@@ -462,8 +463,9 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::FM][C::FN]) {
 // Epilogue through LDS.  After the main loop the operand buffers are free;
 // the accumulators of one row of waves (WTM x BN fp32) are written there in
 // fully unrolled code (32x32 MFMA output layout: element r of a lane sits at
-// column lane % 32, row 8*(r/4) + 4*(lane/32) + r%4 of its 32x32 tile), then every thread walks 8-column pieces of those rows:
-// fn(block_row, block_col, v[8]).  Consecutive lanes take consecutive pieces
+// column lane % 32, row 8*(r/4) + 4*(lane/32) + r%4 of its 32x32 tile), then
+// every thread walks 8-column pieces of those rows: fn(block_row, block_col,
+// v[8]).  Consecutive lanes take consecutive pieces
 // of a row, so 8 aligned lanes cover one 64-column block and global accesses
 // are 16-byte vectors.  Every lane of every wave runs the same number of
 // pieces, so fn may use cross-lane operations within groups of 8 lanes.
