@@ -50,7 +50,7 @@ int64_t chunk_rows(int64_t BT, int64_t H, int64_t V, int64_t chunk_size, int32_t
 // ---------------------------------------------------------- workspace layout
 constexpr int64_t kAlign = 256;
 constexpr uint64_t kMaxOperandBytes = 0x7fff0000ull;  // 2 GiB - 64 KiB
-constexpr int kDxTargetBlocks = 256;     // one workgroup per CU on 256 CUs
+constexpr int kDxCUs = 256;  // split k until every resident workgroup slot of 256 CUs is busy
 constexpr int64_t kDxMinKPerSplit = 1024;
 constexpr int kDxMaxSplits = 32;
 
@@ -95,8 +95,9 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t c, const
   L.ldz = round_up(V, 8);
   L.ldx = round_up(c, 8);
   L.stats_ld = ceil_div(V, stats_cols());
-  const int64_t tiles = ceil_div(c, dx_tile_m((int)c, H)) * ceil_div(H, dx_tile_n((int)c, H));
-  int64_t splits = ceil_div(kDxTargetBlocks, tiles);
+  const DxTile dt = dx_tile((int)c, H);
+  const int64_t tiles = ceil_div(c, dt.bm) * ceil_div(H, dt.bn);
+  int64_t splits = ceil_div((int64_t)kDxCUs * dt.occ, tiles);
   const int64_t by_k = L.ldz / kDxMinKPerSplit;
   if (splits > by_k) splits = by_k;
   if (splits > kDxMaxSplits) splits = kDxMaxSplits;

@@ -27,37 +27,38 @@
 
 namespace flce {
 
-template <int BM_, int BN_>
+// A tile shape: BM x BN outputs per workgroup of 2 x 2 waves, KBYTES bytes
+// of k per LDS row of a k-contiguous operand tile (BK = KBYTES / element
+// size), sized for OCC resident workgroups per CU (OCC waves per SIMD, which
+// caps a wave at 512 / OCC registers).
+template <int BM_, int BN_, int KBYTES_, int OCC_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
+  static constexpr int KBYTES = KBYTES_, OCC = OCC_;
   static constexpr int WAVES_M = 2, WAVES_N = 2;
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
 };
-typedef Cfg<256, 256> Big;
-typedef Cfg<128, 128> Small;
+typedef Cfg<256, 256, 128, 1> Big;
+typedef Cfg<256, 128, 64, 2> Medium;
+typedef Cfg<128, 128, 128, 2> Small;
 
-// k-tile geometry: every LDS row of a k-contiguous tile holds kKBytes bytes
-// of k (BK = 64 bf16/fp16, 32 fp32).  (Measured on MI355X: 128-byte rows
-// beat 64-byte rows, whose extra barriers cost more than their extra stages
-// gain.)
-constexpr int kKBytes = 128;
-// LDS stages per operand, per kernel (measured on MI355X).  A tile is needed
-// S - 1 iterations after its loads are issued, so a third stage doubles the
-// time that operand's loads have to arrive.
-constexpr int kLogitsStagesA = 2, kLogitsStagesB = 3;
-constexpr int kDxStagesA = 3, kDxStagesB = 2;
-constexpr int kDwStagesA = 2, kDwStagesB = 3;
-// Parts each k-tile's loads are split into, spread over the k-steps of the
-// previous tile's MFMA work (1: all issued after the first k-step).
-constexpr int kLogitsParts = 2, kDxParts = 2, kDwParts = 4;
+// LDS stages per operand (SA, SB) and the parts P each k-tile's loads are
+// split into, per kernel and tile shape (measured on MI355X).  A tile is
+// needed S - 1 iterations after its loads are issued, so a third stage
+// doubles the time that operand's loads have to arrive; the parts spread a
+// tile's loads over the k-steps of the previous tile's MFMA work.
+template <class C> struct LogitsPipe { static constexpr int SA = 2, SB = 3, P = 2; };
+template <class C> struct DxPipe { static constexpr int SA = 3, SB = 2, P = 2; };
+template <class C> struct DwPipe { static constexpr int SA = 2, SB = 3, P = 4; };
+template <> struct DwPipe<Medium> { static constexpr int SA = 3, SB = 3, P = 2; };
 
-template <class T>
+template <class T, class C>
 struct KT {
   typedef typename T::storage S;
-  static constexpr int BK = kKBytes / (int)sizeof(S);
-  static constexpr int RB = kKBytes;
+  static constexpr int BK = C::KBYTES / (int)sizeof(S);
+  static constexpr int RB = C::KBYTES;
   static constexpr int STEPS = BK / T::kstep;  // MFMA k-steps per k-tile
 };
 
@@ -132,10 +133,10 @@ __device__ __forceinline__ void wait_and_barrier() {
 // ---------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(4))) short v4i16_t;
 
-template <class T>
+template <class T, int RB_>
 struct RowSwz {
   typedef typename T::storage S;
-  static constexpr int RB = KT<T>::RB;
+  static constexpr int RB = RB_;
   static_assert(RB == 64 || RB == 128, "row swizzle assumes 64- or 128-byte rows");
   static constexpr size_t bytes(int R) { return (size_t)R * RB; }
   // LDS serves 256 bytes per cycle (64 banks): the 16 rows read by 16
@@ -151,12 +152,12 @@ struct RowSwz {
   }
 };
 
-template <class T, int R>
+template <class T, int R, int BK>
 struct ColSwz {
   typedef typename T::storage S;
   static constexpr int RBT = R * (int)sizeof(S);  // bytes per k-row
   static constexpr int EPC = 16 / (int)sizeof(S); // elements per 16-byte chunk
-  static constexpr size_t bytes(int) { return (size_t)KT<T>::BK * RBT; }
+  static constexpr size_t bytes(int) { return (size_t)BK * RBT; }
   // 16-bit: the 4 k-rows of one transposing read move by 64 bytes each
   // (chunk ^= 4 (k % 4)); fp32: odd k-rows move by 128 bytes (chunk ^= 8 (k % 2)).
   static_assert(RBT >= 256, "column swizzle needs 16 chunks per k-row");
@@ -192,12 +193,13 @@ struct ColSwz {
 // L % CPR, i.e. k-chunk (L % CPR) ^ swz(row).  Chunks whose first k is >=
 // kend read as zero; callers keep kend a multiple of the chunk width, and
 // elements between the logical K and kend are zero in memory.
-template <class T, int R, int NWAVES>
+template <class T, class C, int R>
 struct DmaRows {
-  typedef RowSwz<T> Layout;
+  typedef RowSwz<T, C::KBYTES> Layout;
   typedef typename T::storage S;
-  static constexpr int CPR = KT<T>::RB / 16;
-  static constexpr int RPI = 1024 / KT<T>::RB;
+  static constexpr int NWAVES = C::NT / 64;
+  static constexpr int CPR = C::KBYTES / 16;
+  static constexpr int RPI = 1024 / C::KBYTES;
   static constexpr int NI = R / RPI / NWAVES;  // instructions per wave per k-tile
   static_assert(R % (RPI * NWAVES) == 0, "tile rows not divisible among waves");
   static constexpr size_t TILE_BYTES = Layout::bytes(R);
@@ -240,16 +242,18 @@ struct DmaRows {
 // read as zero (chunk granularity).  An instruction fills RPI = 1024 / (R *
 // s) k-rows; lane L takes k-row L / CPRT of its group and physical chunk
 // L % CPRT.
-template <class T, int R, int NWAVES>
+template <class T, class C, int R>
 struct DmaCols {
-  typedef ColSwz<T, R> Layout;
+  typedef ColSwz<T, R, KT<T, C>::BK> Layout;
   typedef typename T::storage S;
+  static constexpr int NWAVES = C::NT / 64;
+  static constexpr int BK = KT<T, C>::BK;
   static constexpr int RBT = Layout::RBT;
   static_assert(RBT <= 1024 && 1024 % RBT == 0, "k-row must divide 1 KiB");
   static constexpr int CPRT = RBT / 16;
   static constexpr int RPI = 1024 / RBT;
-  static constexpr int NI = KT<T>::BK / RPI / NWAVES;
-  static_assert(KT<T>::BK % (RPI * NWAVES) == 0, "k-rows not divisible among waves");
+  static constexpr int NI = BK / RPI / NWAVES;
+  static_assert(BK % (RPI * NWAVES) == 0, "k-rows not divisible among waves");
   static constexpr size_t TILE_BYTES = Layout::bytes(R);
   int krow[NI];      // k-row within the tile of each instruction
   uint32_t cofs[NI]; // byte offset of this lane's column chunk (kOOB: outside)
@@ -290,13 +294,13 @@ struct Smem {
   static constexpr size_t EPI = (size_t)C::WTM * (C::BN + 4) * sizeof(float);
   static constexpr size_t EPI_ALL = EPI + EXTRA;
   static constexpr size_t BYTES = OPERANDS > EPI_ALL ? OPERANDS : EPI_ALL;
-  static_assert(BYTES <= 160 * 1024, "gfx950 LDS per workgroup");
+  static_assert(BYTES * C::OCC <= 160 * 1024, "gfx950 LDS per CU");
 };
 
 // Fragment address helpers: a RowSwz operand is addressed by its row, a
 // ColSwz operand by the first column of the 32-wide MFMA block.
 template <class L> struct IsCol { static constexpr bool value = false; };
-template <class T, int R> struct IsCol<ColSwz<T, R>> { static constexpr bool value = true; };
+template <class T, int R, int BK> struct IsCol<ColSwz<T, R, BK>> { static constexpr bool value = true; };
 
 template <class L>
 __device__ __forceinline__ u32x4_t frag16_of(const unsigned char* b, int blk, int s, int lane) {
@@ -335,7 +339,7 @@ template <class T, class C, class LA, class LB, class DMA>
 __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned char* Bb,
                                          int wm, int wn, int lane,
                                          f32x16_t (&acc)[C::FM][C::FN], DMA dma) {
-  constexpr int STEPS = KT<T>::STEPS;
+  constexpr int STEPS = KT<T, C>::STEPS;
   if constexpr (sizeof(typename T::storage) == 2) {
     u32x4_t fa[2][C::FM], fb[2][C::FN];
     auto fetch = [&](int buf, int s) {
@@ -404,8 +408,8 @@ __device__ __forceinline__ void main_loop(IA ia, IB ib, int nk, unsigned char* s
   typedef typename OA::Layout LA_;
   typedef typename OB::Layout LB_;
   typedef Smem<C, OA, OB, SA, SB> SM;
-  constexpr int BK = KT<T>::BK;
-  constexpr int STEPS = KT<T>::STEPS;
+  constexpr int BK = KT<T, C>::BK;
+  constexpr int STEPS = KT<T, C>::STEPS;
   static_assert(P >= 1 && STEPS % P == 0, "parts must divide the k-steps");
   constexpr int LA = SA - 1, LB = SB - 1;
   constexpr int LEAD = LA > LB ? LA : LB;
@@ -613,11 +617,12 @@ constexpr int kLogitsGroupM = 4, kDxGroupM = 4, kDwGroupN = 8;
 // block) running max and sum of exp, and the target logit in fp32.
 // ---------------------------------------------------------------------------
 template <class T, class C>
-__global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
+__global__ __launch_bounds__(C::NT, C::OCC) void logits_kernel(LogitsArgs a) {
   typedef typename T::storage S;
-  typedef DmaRows<T, C::BM, C::NT / 64> OA;
-  typedef DmaRows<T, C::BN, C::NT / 64> OB;
-  typedef Smem<C, OA, OB, kLogitsStagesA, kLogitsStagesB, C::BM * sizeof(int64_t)> SM;
+  typedef DmaRows<T, C, C::BM> OA;
+  typedef DmaRows<T, C, C::BN> OB;
+  typedef LogitsPipe<C> PI;
+  typedef Smem<C, OA, OB, PI::SA, PI::SB, C::BM * sizeof(int64_t)> SM;
   extern __shared__ __align__(16) unsigned char smem_raw[];
 
   const int tiles_m = (a.rows + C::BM - 1) / C::BM;
@@ -649,11 +654,11 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
   const int K = (int)a.H;
-  constexpr int P = kLogitsParts;
-  main_loop<T, C, OA, OB, kLogitsStagesA, kLogitsStagesB, P>(
+  constexpr int P = PI::P;
+  main_loop<T, C, OA, OB, PI::SA, PI::SB, P>(
       [&](unsigned char* tile, int k0, int p) { la.template issue<P>(xr, tile, k0, K, p); },
       [&](unsigned char* tile, int k0, int p) { lb.template issue<P>(wr, tile, k0, K, p); },
-      (K + KT<T>::BK - 1) / KT<T>::BK, smem_raw, wm, wn, lane, acc);
+      (K + KT<T, C>::BK - 1) / KT<T, C>::BK, smem_raw, wm, wn, lane, acc);
 
   // Epilogue: add the bias (when given; PR #1554, Tests: bias on and off),
   // store the logits, and per (row, 64-column block) the max and the sum of
@@ -742,10 +747,11 @@ __global__ __launch_bounds__(C::NT) void logits_kernel(LogitsArgs a) {
 // or, with splits > 1, fp32 partials part[split][m][n] reduced afterwards.
 // ---------------------------------------------------------------------------
 template <class T, class C>
-__global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
+__global__ __launch_bounds__(C::NT, C::OCC) void dx_kernel(DxArgs a) {
   typedef typename T::storage S;
-  typedef DmaRows<T, C::BM, C::NT / 64> OA;
-  typedef DmaCols<T, C::BN, C::NT / 64> OB;
+  typedef DmaRows<T, C, C::BM> OA;
+  typedef DmaCols<T, C, C::BN> OB;
+  typedef DxPipe<C> PI;
   extern __shared__ __align__(16) unsigned char smem_raw[];
 
   const int tiles_m = (a.rows + C::BM - 1) / C::BM;
@@ -782,22 +788,23 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxArgs a) {
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
   const int K = (int)(kend - kbeg);
-  constexpr int P = kDxParts < KT<T>::STEPS ? kDxParts : KT<T>::STEPS;
-  main_loop<T, C, OA, OB, kDxStagesA, kDxStagesB, P>(
+  constexpr int BK = KT<T, C>::BK;
+  constexpr int P = PI::P < KT<T, C>::STEPS ? PI::P : KT<T, C>::STEPS;
+  main_loop<T, C, OA, OB, PI::SA, PI::SB, P>(
       [&](unsigned char* tile, int k0, int p) { la.template issue<P>(gr, tile, k0, K, p); },
       [&](unsigned char* tile, int k0, int p) {
         // W rows of this k-tile: one descriptor per tile keeps offsets small.
         // (branch-free: a tile past the end gets an empty descriptor)
         const int64_t r0 = kbeg + k0;
         const int64_t left = kend_w - r0;
-        const int nr = left <= 0 ? 0 : (left < KT<T>::BK ? (int)left : KT<T>::BK);
+        const int nr = left <= 0 ? 0 : (left < BK ? (int)left : BK);
         const desc_t wr =
             make_rsrc(W + (left > 0 ? r0 : 0) * H, (uint32_t)nr * w_row_bytes);
         lb.template issue<P>(
             wr, tile, 0, [&](int k) -> uint32_t { return k < nr ? (uint32_t)k * w_row_bytes : kOOB; },
             p);
       },
-      K > 0 ? (K + KT<T>::BK - 1) / KT<T>::BK : 0, smem_raw, wm, wn, lane, acc);
+      K > 0 ? (K + BK - 1) / BK : 0, smem_raw, wm, wn, lane, acc);
 
   const float sc = upstream_scale(a.grad_output, a.inv_n, a.reduction);
   S* dX = static_cast<S*>(a.dX);
@@ -898,10 +905,11 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
 }
 
 template <class T, class C, class D>
-__global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
+__global__ __launch_bounds__(C::NT, C::OCC) void dw_kernel(DwArgs a) {
   typedef typename T::storage S;
-  typedef DmaCols<T, C::BM, C::NT / 64> OA;
-  typedef DmaRows<T, C::BN, C::NT / 64> OB;
+  typedef DmaCols<T, C, C::BM> OA;
+  typedef DmaRows<T, C, C::BN> OB;
+  typedef DwPipe<C> PI;
   extern __shared__ __align__(16) unsigned char smem_raw[];
 
   const int tiles_m = (int)((a.V + C::BM - 1) / C::BM);
@@ -931,12 +939,13 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
 
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
-  constexpr int P = kDwParts < KT<T>::STEPS ? kDwParts : KT<T>::STEPS;
-  main_loop<T, C, OA, OB, kDwStagesA, kDwStagesB, P>(
+  constexpr int BK = KT<T, C>::BK;
+  constexpr int P = PI::P < KT<T, C>::STEPS ? PI::P : KT<T, C>::STEPS;
+  main_loop<T, C, OA, OB, PI::SA, PI::SB, P>(
       [&](unsigned char* tile, int k0, int p) {
         // (branch-free: a tile past the end gets an empty descriptor)
         const int left = a.rows - k0;
-        const int nr = left <= 0 ? 0 : (left < KT<T>::BK ? left : KT<T>::BK);
+        const int nr = left <= 0 ? 0 : (left < BK ? left : BK);
         const desc_t gr =
             make_rsrc(G + (int64_t)(left > 0 ? k0 : 0) * a.ldz, (uint32_t)nr * gz_bytes);
         la.template issue<P>(
@@ -944,7 +953,7 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwArgs a) {
             p);
       },
       [&](unsigned char* tile, int k0, int p) { lb.template issue<P>(xr, tile, k0, a.rows, p); },
-      (a.rows + KT<T>::BK - 1) / KT<T>::BK, smem_raw, wm, wn, lane, acc);
+      (a.rows + BK - 1) / BK, smem_raw, wm, wn, lane, acc);
 
   const float sc = upstream_scale(a.grad_output, a.inv_n, a.reduction);
   const bool accumulate = a.accumulate != 0;
@@ -964,14 +973,14 @@ static hipError_t allow_lds(K kernel, size_t bytes) {
 }
 
 template <class T, class C>
-struct LogitsSmem : Smem<C, DmaRows<T, C::BM, C::NT / 64>, DmaRows<T, C::BN, C::NT / 64>,
-                         kLogitsStagesA, kLogitsStagesB, C::BM * sizeof(int64_t)> {};
+struct LogitsSmem : Smem<C, DmaRows<T, C, C::BM>, DmaRows<T, C, C::BN>, LogitsPipe<C>::SA,
+                         LogitsPipe<C>::SB, C::BM * sizeof(int64_t)> {};
 template <class T, class C>
-struct DxSmem : Smem<C, DmaRows<T, C::BM, C::NT / 64>, DmaCols<T, C::BN, C::NT / 64>,
-                     kDxStagesA, kDxStagesB> {};
+struct DxSmem : Smem<C, DmaRows<T, C, C::BM>, DmaCols<T, C, C::BN>, DxPipe<C>::SA,
+                     DxPipe<C>::SB> {};
 template <class T, class C>
-struct DwSmem : Smem<C, DmaCols<T, C::BM, C::NT / 64>, DmaRows<T, C::BN, C::NT / 64>,
-                     kDwStagesA, kDwStagesB> {};
+struct DwSmem : Smem<C, DmaCols<T, C, C::BM>, DmaRows<T, C, C::BN>, DwPipe<C>::SA,
+                     DwPipe<C>::SB> {};
 
 template <class T, class C>
 static hipError_t launch_logits_t(const LogitsArgs& a, hipStream_t st) {
@@ -998,24 +1007,39 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tile choice.  The big tile needs enough rows and columns to fill it; the
-// grad_weight update with few rows per chunk is bound by the dW
-// read-modify-write, where two resident workgroups per CU hide more latency.
-bool logits_big(int rows, int64_t V) { return rows > 128 && V >= 1024; }
-bool dx_big(int rows, int64_t H) { return rows > 128 && H >= 256; }
-bool dw_big(int rows, int64_t H) { return rows > 256 && H >= 256; }
+// Tile choice.  Big and Medium need enough rows and columns to fill them.
+// grad_weight with 16-bit operands takes Medium: two workgroups per CU, so
+// that one workgroup's dW read-modify-write epilogue overlaps the other's
+// MFMA work (measured on MI355X: 2.60 -> 2.40 ms at chunk 2048, where Medium
+// logits and grad_input are 15-25 % slower than Big: with half the data
+// reuse per wave, their k loops are bound by LDS traffic).  fp32 keeps Big.
+// The grad_weight update with few rows per chunk is bound by the dW
+// read-modify-write, where the small tile's occupancy hides more latency.
+enum class Shape { Small, Medium, Big };
+Shape logits_shape(int rows, int64_t V) { return rows > 128 && V >= 1024 ? Shape::Big : Shape::Small; }
+Shape dx_shape(int rows, int64_t H) { return rows > 128 && H >= 256 ? Shape::Big : Shape::Small; }
+Shape dw_shape(int dtype, int rows, int64_t H) {
+  if (!(rows > 256 && H >= 256)) return Shape::Small;
+  return dtype == 0 ? Shape::Big : Shape::Medium;
+}
 
 template <class T>
 static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
-  return logits_big(a.rows, a.V) ? launch_logits_t<T, Big>(a, st) : launch_logits_t<T, Small>(a, st);
+  return logits_shape(a.rows, a.V) == Shape::Big ? launch_logits_t<T, Big>(a, st)
+                                                 : launch_logits_t<T, Small>(a, st);
 }
 template <class T>
 static hipError_t dx_t(const DxArgs& a, hipStream_t st) {
-  return dx_big(a.rows, a.H) ? launch_dx_t<T, Big>(a, st) : launch_dx_t<T, Small>(a, st);
+  return dx_shape(a.rows, a.H) == Shape::Big ? launch_dx_t<T, Big>(a, st)
+                                             : launch_dx_t<T, Small>(a, st);
 }
 template <class T, class D>
-static hipError_t dw_t(const DwArgs& a, hipStream_t st) {
-  return dw_big(a.rows, a.H) ? launch_dw_t<T, Big, D>(a, st) : launch_dw_t<T, Small, D>(a, st);
+static hipError_t dw_t(int dtype, const DwArgs& a, hipStream_t st) {
+  switch (dw_shape(dtype, a.rows, a.H)) {
+    case Shape::Big: return launch_dw_t<T, Big, D>(a, st);
+    case Shape::Medium: return launch_dw_t<T, Medium, D>(a, st);
+    default: return launch_dw_t<T, Small, D>(a, st);
+  }
 }
 
 hipError_t launch_logits(int dtype, const LogitsArgs& a, hipStream_t st) {
@@ -1030,16 +1054,20 @@ hipError_t launch_dx(int dtype, const DxArgs& a, hipStream_t st) {
 }
 hipError_t launch_dw(int dtype, const DwArgs& a, hipStream_t st) {
   // dW is fp32 or the operand dtype.
-  if (dtype == 0) return dw_t<F32, float>(a, st);
-  if (dtype == 1) return a.dw_dtype == 0 ? dw_t<F16, float>(a, st) : dw_t<F16, F16>(a, st);
-  return a.dw_dtype == 0 ? dw_t<BF16, float>(a, st) : dw_t<BF16, BF16>(a, st);
+  if (dtype == 0) return dw_t<F32, float>(dtype, a, st);
+  if (dtype == 1)
+    return a.dw_dtype == 0 ? dw_t<F16, float>(dtype, a, st) : dw_t<F16, F16>(dtype, a, st);
+  return a.dw_dtype == 0 ? dw_t<BF16, float>(dtype, a, st) : dw_t<BF16, BF16>(dtype, a, st);
 }
 
-int dx_tile_m(int rows, int64_t H) { return dx_big(rows, H) ? Big::BM : Small::BM; }
-int dx_tile_n(int rows, int64_t H) { return dx_big(rows, H) ? Big::BN : Small::BN; }
+DxTile dx_tile(int rows, int64_t H) {
+  return dx_shape(rows, H) == Shape::Big ? DxTile{Big::BM, Big::BN, Big::OCC}
+                                         : DxTile{Small::BM, Small::BN, Small::OCC};
+}
 // Column width of one (max, sum exp) entry written by the logits GEMM.
 int stats_cols() {
-  static_assert(Big::FN % 2 == 0 && Small::FN % 2 == 0, "64-column stats blocks");
+  static_assert(Big::FN % 2 == 0 && Medium::FN % 2 == 0 && Small::FN % 2 == 0,
+                "64-column stats blocks");
   return 64;
 }
 

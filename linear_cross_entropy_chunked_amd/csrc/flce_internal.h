@@ -138,8 +138,12 @@ hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st);
 hipError_t launch_scale_cast(const void* src, int src_dtype, void* dst, int dst_dtype,
                              int64_t n, const float* scale, hipStream_t st);
 
-int dx_tile_m(int rows, int64_t H);
-int dx_tile_n(int rows, int64_t H);
+// grad_input tile shape for a chunk of `rows` rows: bm x bn outputs per
+// workgroup, occ workgroups resident per CU.
+struct DxTile {
+  int bm, bn, occ;
+};
+DxTile dx_tile(int rows, int64_t H);
 int stats_cols();
 
 }  // namespace flce

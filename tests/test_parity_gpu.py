@@ -107,6 +107,26 @@ def test_ragged_fp32(pkg, shape):
     _check(r, ref, "f32", "sum")
 
 
+# ------------------------------------- large tiles: chunks of more than 256 rows
+@pytest.mark.parametrize("dtype,accum", [("bf16", "same"), ("bf16", "f32"), ("f16", "same"),
+                                         ("f16", "f32"), ("f32", "f32")])
+def test_ragged_large_tiles(pkg, dtype, accum):
+    """Chunks of more than 256 labelled rows take the 256-row tiles: logits and
+    grad_input 256 x 256, grad_weight 256 x 128 for 16-bit operands and
+    256 x 256 for fp32.  Every dimension is ragged against them: about 810
+    labelled rows give chunks of 512 and about 300 rows; V = 1100 is four
+    256-column tiles and 76 columns; H = 392 is three 128-column tiles and 8."""
+    BT, H, V, chunk = 900, 392, 1100, 512
+    seed = 2500 + len(dtype)
+    X, W, t = si.make_case(BT, H, V, dtype, seed, ignore="scattered", frac=0.1)
+    g = si.make_grad_output(t, "sum", seed, scalar=0.5)
+    r = _run(pkg, X, W, t, reduction="sum", chunk_size=chunk, grad_output=g,
+             accum_dtype=torch.float32 if accum == "f32" else None)
+    ref = oracle.flce(X, W, t, reduction="sum", grad_output=g)
+    assert r.stats["chunks_run"] == 2 and ref["n_valid"] - chunk > 256
+    _check(r, ref, dtype, "sum")
+
+
 def test_split_grad_input_path(pkg):
     """Few row tiles and a long vocabulary: grad_input runs split over V."""
     BT, H, V = 64, 256, 8192
