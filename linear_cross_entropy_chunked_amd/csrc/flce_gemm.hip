@@ -16,10 +16,11 @@
 // stages per operand: later k-tiles stream in while the current one is
 // multiplied, their loads spread over its MFMA k-steps.
 //
-// Two tile shapes: 256x256 blocks of four 128x128 waves (one workgroup per
-// CU) for the compute-bound shapes, and 128x128 blocks of four 64x64 waves
-// (two workgroups per CU) where the problem is small or, for grad_weight with
-// few rows per chunk, bound by the read-modify-write of dW.
+// Tile shapes: 256x256 blocks (one workgroup per CU) of four 128x128 waves
+// for fp32 operands and of eight 64x128 or 128x64 waves (two per SIMD) for
+// 16-bit operands; 128x128 blocks of four 64x64 waves (two workgroups per
+// CU) where the problem is small or, for grad_weight with few rows per
+// chunk, bound by the read-modify-write of dW.
 #include <type_traits>
 
 #include "flce_device.hpp"
@@ -27,22 +28,25 @@
 
 namespace flce {
 
-// A tile shape: BM x BN outputs per workgroup of 2 x 2 waves, KBYTES bytes
-// of k per LDS row of a k-contiguous operand tile (BK = KBYTES / element
-// size), sized for OCC resident workgroups per CU (OCC waves per SIMD, which
-// caps a wave at 512 / OCC registers).
-template <int BM_, int BN_, int KBYTES_, int OCC_>
+// A tile shape: BM x BN outputs per workgroup of WAVES_M x WAVES_N waves,
+// KBYTES bytes of k per LDS row of a k-contiguous operand tile (BK = KBYTES
+// / element size), sized for WGS resident workgroups per CU.  A CU's four
+// SIMDs then hold WAVES_PER_SIMD waves each, which caps a wave at 512 /
+// WAVES_PER_SIMD registers.
+template <int BM_, int BN_, int KBYTES_, int WGS_, int WAVES_M_ = 2, int WAVES_N_ = 2>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
-  static constexpr int KBYTES = KBYTES_, OCC = OCC_;
-  static constexpr int WAVES_M = 2, WAVES_N = 2;
+  static constexpr int KBYTES = KBYTES_, WGS = WGS_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int WAVES_PER_SIMD = WGS * WAVES_M * WAVES_N / 4;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
 };
-typedef Cfg<256, 256, 128, 1> Big;
-typedef Cfg<256, 128, 64, 2> Medium;
-typedef Cfg<128, 128, 128, 2> Small;
+typedef Cfg<256, 256, 128, 1> Big;         // 4 waves of 128 x 128 (fp32 operands)
+typedef Cfg<256, 256, 128, 1, 4, 2> Big8M;  // 8 waves of 64 x 128 (16-bit logits, grad_weight)
+typedef Cfg<256, 256, 128, 1, 2, 4> Big8N;  // 8 waves of 128 x 64 (16-bit grad_input)
+typedef Cfg<128, 128, 128, 2> Small;        // 4 waves of 64 x 64, 2 workgroups per CU
 
 // LDS stages per operand (SA, SB) and the parts P each k-tile's loads are
 // split into, per kernel and tile shape (measured on MI355X).  A tile is
@@ -50,9 +54,11 @@ typedef Cfg<128, 128, 128, 2> Small;
 // doubles the time that operand's loads have to arrive; the parts spread a
 // tile's loads over the k-steps of the previous tile's MFMA work.
 template <class C> struct LogitsPipe { static constexpr int SA = 2, SB = 3, P = 2; };
+template <> struct LogitsPipe<Big8M> { static constexpr int SA = 2, SB = 3, P = 1; };
 template <class C> struct DxPipe { static constexpr int SA = 3, SB = 2, P = 2; };
+template <> struct DxPipe<Big8N> { static constexpr int SA = 2, SB = 3, P = 1; };
 template <class C> struct DwPipe { static constexpr int SA = 2, SB = 3, P = 4; };
-template <> struct DwPipe<Medium> { static constexpr int SA = 3, SB = 3, P = 2; };
+template <> struct DwPipe<Big8M> { static constexpr int SA = 3, SB = 2, P = 1; };
 
 template <class T, class C>
 struct KT {
@@ -294,7 +300,7 @@ struct Smem {
   static constexpr size_t EPI = (size_t)C::WTM * (C::BN + 4) * sizeof(float);
   static constexpr size_t EPI_ALL = EPI + EXTRA;
   static constexpr size_t BYTES = OPERANDS > EPI_ALL ? OPERANDS : EPI_ALL;
-  static_assert(BYTES * C::OCC <= 160 * 1024, "gfx950 LDS per CU");
+  static_assert(BYTES * C::WGS <= 160 * 1024, "gfx950 LDS per CU");
 };
 
 // Fragment address helpers: a RowSwz operand is addressed by its row, a
@@ -617,7 +623,7 @@ constexpr int kLogitsGroupM = 4, kDxGroupM = 4, kDwGroupN = 8;
 // block) running max and sum of exp, and the target logit in fp32.
 // ---------------------------------------------------------------------------
 template <class T, class C>
-__global__ __launch_bounds__(C::NT, C::OCC) void logits_kernel(LogitsArgs a) {
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(LogitsArgs a) {
   typedef typename T::storage S;
   typedef DmaRows<T, C, C::BM> OA;
   typedef DmaRows<T, C, C::BN> OB;
@@ -747,7 +753,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void logits_kernel(LogitsArgs a) {
 // or, with splits > 1, fp32 partials part[split][m][n] reduced afterwards.
 // ---------------------------------------------------------------------------
 template <class T, class C>
-__global__ __launch_bounds__(C::NT, C::OCC) void dx_kernel(DxArgs a) {
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void dx_kernel(DxArgs a) {
   typedef typename T::storage S;
   typedef DmaRows<T, C, C::BM> OA;
   typedef DmaCols<T, C, C::BN> OB;
@@ -905,7 +911,7 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
 }
 
 template <class T, class C, class D>
-__global__ __launch_bounds__(C::NT, C::OCC) void dw_kernel(DwArgs a) {
+__global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void dw_kernel(DwArgs a) {
   typedef typename T::storage S;
   typedef DmaCols<T, C, C::BM> OA;
   typedef DmaRows<T, C, C::BN> OB;
@@ -1007,39 +1013,41 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tile choice.  Big and Medium need enough rows and columns to fill them.
-// grad_weight with 16-bit operands takes Medium: two workgroups per CU, so
-// that one workgroup's dW read-modify-write epilogue overlaps the other's
-// MFMA work (measured on MI355X: 2.60 -> 2.40 ms at chunk 2048, where Medium
-// logits and grad_input are 15-25 % slower than Big: with half the data
-// reuse per wave, their k loops are bound by LDS traffic).  fp32 keeps Big.
+// Tile choice.  The 256-row tiles need enough rows and columns to fill
+// them.  With 16-bit operands the three GEMMs take eight waves on the
+// 256 x 256 tile, two per SIMD, so that one wave's waits for LDS, loads and
+// barriers and the epilogue's memory traffic overlap the other wave's MFMA
+// work.  Measured on MI355X at chunk 2048 (interleaved runs of the
+// alternatives): logits 2.23 -> 1.86 ms (64 x 128 wave tiles, loads issued
+// in one part), grad_input 1.92 -> 1.73 ms (128 x 64 wave tiles), grad_weight
+// 2.60 -> 2.32 ms (64 x 128, three stages of G).  256 x 128 tiles with two
+// workgroups per CU reached 2.40 ms for grad_weight but were 15-25 % slower
+// for logits and grad_input, whose k loops they leave bound by LDS traffic
+// (half the operand reuse per workgroup).  fp32 keeps the four-wave tile.
 // The grad_weight update with few rows per chunk is bound by the dW
 // read-modify-write, where the small tile's occupancy hides more latency.
-enum class Shape { Small, Medium, Big };
+enum class Shape { Small, Big };
 Shape logits_shape(int rows, int64_t V) { return rows > 128 && V >= 1024 ? Shape::Big : Shape::Small; }
 Shape dx_shape(int rows, int64_t H) { return rows > 128 && H >= 256 ? Shape::Big : Shape::Small; }
-Shape dw_shape(int dtype, int rows, int64_t H) {
-  if (!(rows > 256 && H >= 256)) return Shape::Small;
-  return dtype == 0 ? Shape::Big : Shape::Medium;
-}
+Shape dw_shape(int rows, int64_t H) { return rows > 256 && H >= 256 ? Shape::Big : Shape::Small; }
 
 template <class T>
 static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
-  return logits_shape(a.rows, a.V) == Shape::Big ? launch_logits_t<T, Big>(a, st)
+  typedef typename std::conditional<sizeof(typename T::storage) == 2, Big8M, Big>::type L;
+  return logits_shape(a.rows, a.V) == Shape::Big ? launch_logits_t<T, L>(a, st)
                                                  : launch_logits_t<T, Small>(a, st);
 }
 template <class T>
 static hipError_t dx_t(const DxArgs& a, hipStream_t st) {
-  return dx_shape(a.rows, a.H) == Shape::Big ? launch_dx_t<T, Big>(a, st)
+  typedef typename std::conditional<sizeof(typename T::storage) == 2, Big8N, Big>::type L;
+  return dx_shape(a.rows, a.H) == Shape::Big ? launch_dx_t<T, L>(a, st)
                                              : launch_dx_t<T, Small>(a, st);
 }
 template <class T, class D>
-static hipError_t dw_t(int dtype, const DwArgs& a, hipStream_t st) {
-  switch (dw_shape(dtype, a.rows, a.H)) {
-    case Shape::Big: return launch_dw_t<T, Big, D>(a, st);
-    case Shape::Medium: return launch_dw_t<T, Medium, D>(a, st);
-    default: return launch_dw_t<T, Small, D>(a, st);
-  }
+static hipError_t dw_t(const DwArgs& a, hipStream_t st) {
+  typedef typename std::conditional<sizeof(typename T::storage) == 2, Big8M, Big>::type L;
+  return dw_shape(a.rows, a.H) == Shape::Big ? launch_dw_t<T, L, D>(a, st)
+                                             : launch_dw_t<T, Small, D>(a, st);
 }
 
 hipError_t launch_logits(int dtype, const LogitsArgs& a, hipStream_t st) {
@@ -1054,19 +1062,20 @@ hipError_t launch_dx(int dtype, const DxArgs& a, hipStream_t st) {
 }
 hipError_t launch_dw(int dtype, const DwArgs& a, hipStream_t st) {
   // dW is fp32 or the operand dtype.
-  if (dtype == 0) return dw_t<F32, float>(dtype, a, st);
-  if (dtype == 1)
-    return a.dw_dtype == 0 ? dw_t<F16, float>(dtype, a, st) : dw_t<F16, F16>(dtype, a, st);
-  return a.dw_dtype == 0 ? dw_t<BF16, float>(dtype, a, st) : dw_t<BF16, BF16>(dtype, a, st);
+  if (dtype == 0) return dw_t<F32, float>(a, st);
+  if (dtype == 1) return a.dw_dtype == 0 ? dw_t<F16, float>(a, st) : dw_t<F16, F16>(a, st);
+  return a.dw_dtype == 0 ? dw_t<BF16, float>(a, st) : dw_t<BF16, BF16>(a, st);
 }
 
 DxTile dx_tile(int rows, int64_t H) {
-  return dx_shape(rows, H) == Shape::Big ? DxTile{Big::BM, Big::BN, Big::OCC}
-                                         : DxTile{Small::BM, Small::BN, Small::OCC};
+  static_assert(Big::BM == Big8N::BM && Big::BN == Big8N::BN && Big::WGS == Big8N::WGS,
+                "both large grad_input tiles split k alike");
+  return dx_shape(rows, H) == Shape::Big ? DxTile{Big::BM, Big::BN, Big::WGS}
+                                         : DxTile{Small::BM, Small::BN, Small::WGS};
 }
 // Column width of one (max, sum exp) entry written by the logits GEMM.
 int stats_cols() {
-  static_assert(Big::FN % 2 == 0 && Medium::FN % 2 == 0 && Small::FN % 2 == 0,
+  static_assert(Big::FN % 2 == 0 && Big8M::FN % 2 == 0 && Small::FN % 2 == 0,
                 "64-column stats blocks");
   return 64;
 }

@@ -139,9 +139,9 @@ hipError_t launch_scale_cast(const void* src, int src_dtype, void* dst, int dst_
                              int64_t n, const float* scale, hipStream_t st);
 
 // grad_input tile shape for a chunk of `rows` rows: bm x bn outputs per
-// workgroup, occ workgroups resident per CU.
+// workgroup, wgs workgroups resident per CU.
 struct DxTile {
-  int bm, bn, occ;
+  int bm, bn, wgs;
 };
 DxTile dx_tile(int rows, int64_t H);
 int stats_cols();

@@ -111,11 +111,11 @@ def test_ragged_fp32(pkg, shape):
 @pytest.mark.parametrize("dtype,accum", [("bf16", "same"), ("bf16", "f32"), ("f16", "same"),
                                          ("f16", "f32"), ("f32", "f32")])
 def test_ragged_large_tiles(pkg, dtype, accum):
-    """Chunks of more than 256 labelled rows take the 256-row tiles: logits and
-    grad_input 256 x 256, grad_weight 256 x 128 for 16-bit operands and
-    256 x 256 for fp32.  Every dimension is ragged against them: about 810
-    labelled rows give chunks of 512 and about 300 rows; V = 1100 is four
-    256-column tiles and 76 columns; H = 392 is three 128-column tiles and 8."""
+    """Chunks of more than 256 labelled rows take the 256 x 256 tiles of all
+    three GEMMs (eight waves for 16-bit operands, four for fp32).  Every
+    dimension is ragged against them: about 810 labelled rows give chunks of
+    512 and about 300 rows; V = 1100 is four 256-column tiles and 76 columns;
+    H = 392 is one 256-column tile and 136 columns."""
     BT, H, V, chunk = 900, 392, 1100, 512
     seed = 2500 + len(dtype)
     X, W, t = si.make_case(BT, H, V, dtype, seed, ignore="scattered", frac=0.1)
