@@ -138,12 +138,18 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None):
         step()
     torch.cuda.synchronize()
     log(f"{name}: {steps} timed step(s)")
+    # per-step HIP events on the library's stream, for the step-time spread
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     pkg.flce_profile_begin()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         step()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    pct = lambda q: step_ms[min(len(step_ms) - 1, int(round(q * (len(step_ms) - 1))))]
     prof = pkg.flce_profile_end()
     peak_transient = torch.cuda.max_memory_allocated(dev) - mem0
     del ws
@@ -155,6 +161,7 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None):
         reduction=cfg["reduction"], frozen_weight=frozen, labelled_share=cfg["share"],
         chunk_size=st.chunk_size, chunks_run=st.chunks_run, dx_splits=st.dx_splits,
         n_valid=n_lab, ms_per_step=ms, tokens_per_s=BT * steps / elapsed,
+        step_ms_p20_p50_p80=[pct(0.2), pct(0.5), pct(0.8)],
         algorithmic_tflops=flops / (ms * 1e-3) / 1e12,
         mfma_frac=flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[cfg["dtype"]],
         workspace_bytes=wsb, peak_transient_bytes=int(peak_transient),

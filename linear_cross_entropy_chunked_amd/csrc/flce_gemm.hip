@@ -225,6 +225,25 @@ struct DmaRows {
       kc_el[i] = ((lane % CPR) ^ Layout::swz(row)) * T::vec;
     }
   }
+  // Rows found through a table: read(row) reads the table entry of every
+  // row this lane loads, all reads in flight together, then off(row, entry)
+  // turns each entry into the row's byte offset.
+  template <class ReadFn, class OffFn>
+  __device__ __forceinline__ void init_indexed(int tid, ReadFn read, OffFn off) {
+    const int lane = tid & 63;
+    wave = tid >> 6;
+    const int rin = lane / CPR;
+    uint32_t e[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) e[i] = read((wave + i * NWAVES) * RPI + rin);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      asm volatile("" : "+v"(e[i]));  // the reads stay unconditional and together
+      const int row = (wave + i * NWAVES) * RPI + rin;
+      roff[i] = off(row, e[i]);
+      kc_el[i] = ((lane % CPR) ^ Layout::swz(row)) * T::vec;
+    }
+  }
   // Part `part` of P: the instructions i with i * P / NI == part (P parts
   // spread the tile's loads over the P k-steps of the previous tile).
   template <int P>
@@ -651,11 +670,28 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
   const desc_t wr = make_rsrc(W + n0 * a.H, (uint64_t)nrows_w * a.H * sizeof(S));
   OA la;
   OB lb;
-  la.init(tid, [&](int r) -> uint32_t {
-    const int gm = m0 + r;
-    return gm < a.rows ? (uint32_t)a.idx[gm] * row_bytes : kOOB;
-  });
+  // The block's target columns are read now, so that the two dependent
+  // global reads complete under the k loop, and staged in LDS for the
+  // epilogue afterwards.  Table entries are read unconditionally (row 0 of
+  // the chunk stands in for rows past its end), so that no read waits in a
+  // branch of its own.
+  constexpr int TPT = (C::BM + C::NT - 1) / C::NT;  // target rows per thread
+  int tix[TPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int m = tid + i * C::NT, gm = m0 + m;
+    tix[i] = a.idx[m < C::BM && gm < a.rows ? gm : 0];
+  }
+  la.init_indexed(
+      tid, [&](int r) -> uint32_t { return (uint32_t)a.idx[m0 + r < a.rows ? m0 + r : 0]; },
+      [&](int r, uint32_t e) -> uint32_t { return m0 + r < a.rows ? e * row_bytes : kOOB; });
   lb.init(tid, [&](int r) -> uint32_t { return r < nrows_w ? (uint32_t)r * row_bytes : kOOB; });
+  int64_t tgt[TPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    asm volatile("" : "+v"(tix[i]));
+    tgt[i] = a.targets[tix[i]];
+  }
 
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
@@ -672,13 +708,14 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
   // holding that max.  Both tile shapes reduce a 64-column block the same way
   // (8 lanes x 8 values), so a row's log-sum-exp does not depend on the
   // chunking.
-  // The block's target columns, after the staging area (the operand stages
-  // are free once the main loop is done; the epilogue's first barrier
+  // The block's target columns go after the staging area (the operand
+  // stages are free once the main loop is done; the epilogue's first barrier
   // publishes them).
   int64_t* tgt_s = reinterpret_cast<int64_t*>(smem_raw + SM::EPI);
-  for (int m = tid; m < C::BM; m += C::NT) {
-    const int gm = m0 + m;
-    tgt_s[m] = gm < a.rows ? a.targets[a.idx[gm]] : -1;
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int m = tid + i * C::NT;
+    if (m < C::BM) tgt_s[m] = m0 + m < a.rows ? tgt[i] : -1;
   }
   S* slab = static_cast<S*>(a.slab);
   float2* stats = reinterpret_cast<float2*>(a.stats);
