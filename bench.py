@@ -209,7 +209,25 @@ def cpu_baseline(host, cfg, rows):
     return dict(value=rows / dt, unit="tokens/s", cores=oracle.threads(), kind="oracle",
                 sample=f"first {rows} of {cfg['BT']} rows of the same batch through the fp64 "
                        f"loop oracle (forward + backward, full H={cfg['H']}, V={cfg['V']}); "
-                       f"{dt:.1f} s; widening the inputs to fp64 is not timed")
+                       f"{dt:.1f} s; widening the inputs to fp64 is not timed; host: "
+                       f"{host_description()}")
+
+
+def host_description() -> str:
+    """CPU model and RAM of the machine the oracle runs on (Linux /proc)."""
+    model, ram = "unknown CPU", "unknown RAM"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                ram = f"{int(line.split()[1]) / 2**20:.0f} GiB RAM"
+                break
+    except OSError:
+        pass
+    return f"{model}, {ram}"
 
 
 # ---------------------------------------------------------------- profiling
