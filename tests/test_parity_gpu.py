@@ -127,6 +127,24 @@ def test_ragged_large_tiles(pkg, dtype, accum):
     _check(r, ref, dtype, "sum")
 
 
+@pytest.mark.parametrize("dtype,shape", [("bf16", (300, 256, 1000, 64)), ("bf16", (900, 392, 1100, 512)),
+                                         ("f16", (900, 392, 1100, 512)), ("f32", (900, 392, 1100, 512)),
+                                         ("f32", (300, 256, 1000, 64))])
+def test_repeated_calls_are_bit_identical(pkg, dtype, shape):
+    """Every tile path (128x128; eight-wave 256x256 for 16-bit operands;
+    four-wave 256x256 for fp32) gives bit-identical loss, dX and dW on repeated
+    calls.  The reductions run in a fixed order, so any difference means a
+    race, e.g. an LDS stage read before its loads have landed."""
+    BT, H, V, chunk = shape
+    X, W, t = si.make_case(BT, H, V, dtype, 2600 + BT, ignore="scattered", frac=0.1)
+    runs = [_run(pkg, X, W, t, reduction="mean", chunk_size=chunk, accum_dtype=torch.float32)
+            for _ in range(3)]
+    for r in runs[1:]:
+        assert torch.equal(r.loss, runs[0].loss)
+        assert torch.equal(r.dX, runs[0].dX)
+        assert torch.equal(r.dW, runs[0].dW)
+
+
 def test_split_grad_input_path(pkg):
     """Few row tiles and a long vocabulary: grad_input runs split over V."""
     BT, H, V = 64, 256, 8192
