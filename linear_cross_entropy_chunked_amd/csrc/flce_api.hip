@@ -95,7 +95,7 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t c, const
   L.ldz = round_up(V, 8);
   L.ldx = round_up(c, 8);
   L.stats_ld = ceil_div(V, stats_cols());
-  const DxTile dt = dx_tile((int)c, H);
+  const DxTile dt = dx_tile(dtype, (int)c, H);
   const int64_t tiles = ceil_div(c, dt.bm) * ceil_div(H, dt.bn);
   int64_t splits = ceil_div((int64_t)kDxCUs * dt.wgs, tiles);
   const int64_t by_k = L.ldz / kDxMinKPerSplit;

@@ -1061,12 +1061,21 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t st) {
 // workgroups per CU reached 2.40 ms for grad_weight but were 15-25 % slower
 // for logits and grad_input, whose k loops they leave bound by LDS traffic
 // (half the operand reuse per workgroup).  fp32 keeps the four-wave tile.
-// The grad_weight update with few rows per chunk is bound by the dW
-// read-modify-write, where the small tile's occupancy hides more latency.
+// For 16-bit operands grad_input and grad_weight take the eight-wave tile at
+// any chunk size ("wide"): with few rows per chunk, where the dW
+// read-modify-write bounds grad_weight, a 256 x 256 tile moves four times the
+// bytes per load round trip of a 128 x 128 one (grad_weight at chunk 256:
+// 0.95 -> 0.89 ms with fp32 dW, 2.24 -> 1.72 ms with bf16 dW at H 5376,
+// V 262144; at chunk 128 both GEMMs 9-12 % faster).  Logits keep the
+// 128 x 128 tile for chunks of at most 128 rows (7-11 % faster there).
 enum class Shape { Small, Big };
 Shape logits_shape(int rows, int64_t V) { return rows > 128 && V >= 1024 ? Shape::Big : Shape::Small; }
-Shape dx_shape(int rows, int64_t H) { return rows > 128 && H >= 256 ? Shape::Big : Shape::Small; }
-Shape dw_shape(int rows, int64_t H) { return rows > 256 && H >= 256 ? Shape::Big : Shape::Small; }
+Shape dx_shape(int rows, int64_t H, bool wide) {
+  return (wide || rows > 128) && H >= 256 ? Shape::Big : Shape::Small;
+}
+Shape dw_shape(int rows, int64_t H, bool wide) {
+  return (wide || rows > 256) && H >= 256 ? Shape::Big : Shape::Small;
+}
 
 template <class T>
 static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
@@ -1076,15 +1085,17 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
 }
 template <class T>
 static hipError_t dx_t(const DxArgs& a, hipStream_t st) {
-  typedef typename std::conditional<sizeof(typename T::storage) == 2, Big8N, Big>::type L;
-  return dx_shape(a.rows, a.H) == Shape::Big ? launch_dx_t<T, L>(a, st)
-                                             : launch_dx_t<T, Small>(a, st);
+  constexpr bool k16 = sizeof(typename T::storage) == 2;
+  typedef typename std::conditional<k16, Big8N, Big>::type L;
+  return dx_shape(a.rows, a.H, k16) == Shape::Big ? launch_dx_t<T, L>(a, st)
+                                                  : launch_dx_t<T, Small>(a, st);
 }
 template <class T, class D>
 static hipError_t dw_t(const DwArgs& a, hipStream_t st) {
-  typedef typename std::conditional<sizeof(typename T::storage) == 2, Big8M, Big>::type L;
-  return dw_shape(a.rows, a.H) == Shape::Big ? launch_dw_t<T, L, D>(a, st)
-                                             : launch_dw_t<T, Small, D>(a, st);
+  constexpr bool k16 = sizeof(typename T::storage) == 2;
+  typedef typename std::conditional<k16, Big8M, Big>::type L;
+  return dw_shape(a.rows, a.H, k16) == Shape::Big ? launch_dw_t<T, L, D>(a, st)
+                                                  : launch_dw_t<T, Small, D>(a, st);
 }
 
 hipError_t launch_logits(int dtype, const LogitsArgs& a, hipStream_t st) {
@@ -1104,11 +1115,11 @@ hipError_t launch_dw(int dtype, const DwArgs& a, hipStream_t st) {
   return a.dw_dtype == 0 ? dw_t<BF16, float>(a, st) : dw_t<BF16, BF16>(a, st);
 }
 
-DxTile dx_tile(int rows, int64_t H) {
+DxTile dx_tile(int dtype, int rows, int64_t H) {
   static_assert(Big::BM == Big8N::BM && Big::BN == Big8N::BN && Big::WGS == Big8N::WGS,
                 "both large grad_input tiles split k alike");
-  return dx_shape(rows, H) == Shape::Big ? DxTile{Big::BM, Big::BN, Big::WGS}
-                                         : DxTile{Small::BM, Small::BN, Small::WGS};
+  return dx_shape(rows, H, dtype != 0) == Shape::Big ? DxTile{Big::BM, Big::BN, Big::WGS}
+                                                     : DxTile{Small::BM, Small::BN, Small::WGS};
 }
 // Column width of one (max, sum exp) entry written by the logits GEMM.
 int stats_cols() {

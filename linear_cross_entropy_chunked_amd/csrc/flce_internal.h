@@ -143,7 +143,7 @@ hipError_t launch_scale_cast(const void* src, int src_dtype, void* dst, int dst_
 struct DxTile {
   int bm, bn, wgs;
 };
-DxTile dx_tile(int rows, int64_t H);
+DxTile dx_tile(int dtype, int rows, int64_t H);
 int stats_cols();
 
 }  // namespace flce
