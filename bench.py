@@ -53,6 +53,12 @@ WORKLOADS = {
                                                  accum="same", reduction="sum", chunk=0, share=s,
                                                  seed=1004, frozen=(mode == "frozen"))
        for s in (1.0, 0.75, 0.5, 0.1) for mode in ("trained", "frozen")},
+    # the same, as 8 packed sequences of 1024 tokens, each prompt-first
+    **{f"masked_sft_packed_{int(s * 100)}_{mode}": dict(BT=8192, H=2048, V=151936, dtype="bf16",
+                                                        accum="same", reduction="sum", chunk=0,
+                                                        share=s, seed=1004, seq_len=1024,
+                                                        frozen=(mode == "frozen"))
+       for s in (0.75, 0.5, 0.1) for mode in ("trained", "frozen")},
 }
 
 
@@ -98,7 +104,7 @@ def make_inputs(cfg, dev):
         t = si.make_targets(BT, V, cfg["seed"])
     else:
         t = si.make_targets(BT, V, cfg["seed"], ignore="prompt_first", frac=1.0 - share,
-                            seq_len=BT)
+                            seq_len=cfg.get("seq_len", BT))
     host = (X, W, t)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
     return host, (X.to(dev), W.to(dev), t.to(dev))
@@ -159,7 +165,7 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None):
     res = dict(
         workload=name, BT=BT, H=H, V=V, dtype=cfg["dtype"], accum_dtype=cfg["accum"],
         reduction=cfg["reduction"], frozen_weight=frozen, labelled_share=cfg["share"],
-        chunk_size=st.chunk_size, chunks_run=st.chunks_run, dx_splits=st.dx_splits,
+        seq_len=cfg.get("seq_len", BT), chunk_size=st.chunk_size, chunks_run=st.chunks_run, dx_splits=st.dx_splits,
         n_valid=n_lab, ms_per_step=ms, tokens_per_s=BT * steps / elapsed,
         step_ms_p20_p50_p80=[pct(0.2), pct(0.5), pct(0.8)],
         algorithmic_tflops=flops / (ms * 1e-3) / 1e12,
@@ -420,7 +426,7 @@ def main():
         "config": {"workload": a.workload, "BT": cfg["BT"], "H": cfg["H"], "V": cfg["V"],
                    "chunk_size": main_res["chunk_size"], "accum_dtype": cfg["accum"],
                    "reduction": cfg["reduction"], "labelled_share": cfg["share"],
-                   "frozen_weight": main_res["frozen_weight"]},
+                   "seq_len": main_res["seq_len"], "frozen_weight": main_res["frozen_weight"]},
         "mfma_frac_of_peak": main_res["mfma_frac"],
         "algorithmic_tflops": main_res["algorithmic_tflops"],
         "roofline": rl,

@@ -28,7 +28,8 @@ GOLD = os.path.join(os.path.dirname(__file__), "golden", "full_size")
 TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-3, 2e-2), "f16": (2e-3, 2e-2)}
 TD = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
-# (case id, golden set, BT used, chunk_size, accum, reduction, labelled share, frozen)
+# (case id, golden set, BT used, chunk_size, accum, reduction, labelled share, frozen[,
+#  sequence length of the packed sequences; default one sequence of BT])
 CASES = [
     ("llama_c2048", "llama3_8b_lm_head", 8192, 2048, "f32", "mean", 1.0, False),
     ("llama_c256", "llama3_8b_lm_head", 8192, 256, "f32", "mean", 1.0, False),
@@ -45,6 +46,8 @@ CASES = [
     ("sft_10_trained_sum", "masked_sft", 8192, 0, "same", "sum", 0.1, False),
     ("sft_75_frozen_none", "masked_sft", 8192, 0, "same", "none", 0.75, True),
     ("sft_10_frozen_none", "masked_sft", 8192, 0, "same", "none", 0.1, True),
+    ("sft_50_packed_trained_sum", "masked_sft", 8192, 0, "same", "sum", 0.5, False, 1024),
+    ("sft_75_packed_frozen_none", "masked_sft", 8192, 0, "same", "none", 0.75, True, 1024),
 ]
 
 _cache = {}
@@ -80,14 +83,16 @@ def pkg(flce_lib):
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_full_size(pkg, case):
-    cid, gset, BT, chunk, accum, red, share, frozen = case
+    cid, gset, BT, chunk, accum, red, share, frozen = case[:8]
+    seq = case[8] if len(case) > 8 else BT
     c, BT = _inputs(gset, BT)
     dt = c["dt"]
     tl, tg = TOL[dt]
     X, W = c["X"][:BT], c["W"]
     t = c["t"][:BT].clone()
-    if share < 1.0:  # masked SFT: the first (1 - share) of the sequence is ignored
-        t[: int(round((1.0 - share) * BT))] = -100
+    if share < 1.0:  # masked SFT: the first (1 - share) of each sequence is ignored
+        for s0 in range(0, BT, seq):
+            t[s0:s0 + int(round((1.0 - share) * min(seq, BT - s0)))] = -100
     Xd, Wd = c["Xd"][:BT], c["Wd"]
     lse = c["lse"][:BT].copy()
     lab = (t != -100).numpy()
@@ -95,7 +100,7 @@ def test_full_size(pkg, case):
     N = int(lab.sum())
     g = si.make_grad_output(t, red, c["seed"], scalar=1.0) if red == "none" else None
     print(f"[{cid}] BT={BT} H={X.shape[1]} V={W.shape[0]} {dt} chunk={chunk} {red} "
-          f"share={share} frozen={frozen}", flush=True)
+          f"share={share} seq={seq} frozen={frozen}", flush=True)
 
     dev = torch.device("cuda:0")
     r = pkg.fused_linear_cross_entropy_fwd_bwd(
