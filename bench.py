@@ -53,6 +53,12 @@ WORKLOADS = {
                                                  accum="same", reduction="sum", chunk=0, share=s,
                                                  seed=1004, frozen=(mode == "frozen"))
        for s in (1.0, 0.75, 0.5, 0.1) for mode in ("trained", "frozen")},
+    # reduction none: a per-token upstream gradient in [0.5, 1.5), NaN at ignored rows
+    **{f"masked_sft_{int(s * 100)}_{mode}_none": dict(BT=8192, H=2048, V=151936, dtype="bf16",
+                                                      accum="same", reduction="none", chunk=0,
+                                                      share=s, seed=1004,
+                                                      frozen=(mode == "frozen"))
+       for s in (1.0, 0.75, 0.5, 0.1) for mode in ("trained", "frozen")},
     # the same, as 8 packed sequences of 1024 tokens, each prompt-first
     **{f"masked_sft_packed_{int(s * 100)}_{mode}": dict(BT=8192, H=2048, V=151936, dtype="bf16",
                                                         accum="same", reduction="sum", chunk=0,
@@ -113,6 +119,7 @@ def make_inputs(cfg, dev):
 def run_workload(name, cfg, steps, warmup, dev, host_dev=None):
     import torch
     import linear_cross_entropy_chunked_amd as pkg
+    import synthetic_inputs as si
     BT, H, V = cfg["BT"], cfg["H"], cfg["V"]
     host, (X, W, t) = host_dev if host_dev is not None else make_inputs(cfg, dev)
     dt = {"bf16": pkg.BF16, "f16": pkg.F16, "f32": pkg.F32}[cfg["dtype"]]
@@ -121,6 +128,8 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None):
     red = pkg.REDUCTIONS[cfg["reduction"]]
     tdt = {pkg.F32: torch.float32, pkg.F16: torch.float16, pkg.BF16: torch.bfloat16}
     loss = torch.empty(BT if red == pkg.NONE else 1, dtype=torch.float32, device=dev)
+    gout = (si.make_grad_output(host[2], "none", cfg["seed"]).to(dev) if red == pkg.NONE
+            else None)
     dX = torch.empty_like(X)
     dW = None if frozen else torch.empty(V, H, dtype=tdt[adt], device=dev)
     torch.cuda.synchronize()
@@ -133,7 +142,8 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None):
 
     def step():
         rc = pkg.flce_fwd_bwd(X.data_ptr(), W.data_ptr(), t.data_ptr(), BT, H, V, dt, -100, red,
-                              cfg["chunk"], 1, adt, int(frozen), 0, None, loss.data_ptr(),
+                              cfg["chunk"], 1, adt, int(frozen), 0,
+                              None if gout is None else gout.data_ptr(), loss.data_ptr(),
                               dX.data_ptr(), None if frozen else dW.data_ptr(), ws.data_ptr(),
                               wsb, stream.cuda_stream, st)
         if rc != 0:
