@@ -211,6 +211,29 @@ def test_all_rows_ignored_and_empty_batch(pkg):
     assert float(r.loss) == 0.0 and (r.dW == 0).all()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 8, 1, 16), (5, 8, 3, 16), (3, 16, 65, 16), (33, 8, 1000, 16),
+                                   (257, 264, 1025, 512), (40, 8, 4097, 0)])
+def test_degenerate_shapes(pkg, dtype, shape):
+    """Smallest legal sizes and block edges: one row, H = 8 (the minimum), V = 1,
+    V one column past a 64-column statistics block, 257 rows (one past a
+    256-row tile), the heuristic chunk.  With V = 1 the loss is exactly 0 and,
+    for fp32, so are both gradients; 16-bit operands keep the logits in the
+    operand dtype, so their gradient exp(z - lse) - 1 is of the size of the
+    rounding of z, which the absolute check of _check bounds."""
+    BT, H, V, chunk = shape
+    X, W, t = si.make_case(BT, H, V, dtype, 2700 + BT + V)
+    g = si.make_grad_output(t, "sum", 2700, scalar=1.25)
+    r = _run(pkg, X, W, t, reduction="sum", chunk_size=chunk or None, grad_output=g,
+             accum_dtype=torch.float32)
+    ref = oracle.flce(X, W, t, reduction="sum", grad_output=g)
+    if V == 1:
+        assert float(r.loss) == 0.0 and ref["loss"] == 0.0
+        if dtype == "f32":
+            assert (r.dX == 0).all() and (r.dW == 0).all()
+    _check(r, ref, dtype, "sum")
+
+
 def test_ignored_rows_skip_whole_chunks_only(pkg):
     """40 rows at chunk 16: 0/1/8/24/40 ignored rows give 3/3/2/1/0 chunks run."""
     BT, H, V = 40, 64, 256
