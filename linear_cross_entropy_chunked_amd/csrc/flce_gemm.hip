@@ -42,6 +42,12 @@ struct Cfg {
   static constexpr int WAVES_PER_SIMD = WGS * WAVES_M * WAVES_N / 4;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
+  // Rows of waves whose accumulators one epilogue pass stages in LDS: two for
+  // the 64-row waves of the eight-wave tiles (half the passes, so half the
+  // load round trips of grad_weight's read-modify-write; with bf16 dW at chunk
+  // 256 that is 1.69 -> 1.53 ms).
+  static constexpr int EPI_WROWS = WAVES_M >= 4 ? 2 : 1;
+  static constexpr int EPI_ROWS = EPI_WROWS * WTM;
 };
 typedef Cfg<256, 256, 128, 1> Big;         // 4 waves of 128 x 128 (fp32 operands)
 typedef Cfg<256, 256, 128, 1, 4, 2> Big8M;  // 8 waves of 64 x 128 (16-bit logits, grad_weight)
@@ -309,14 +315,14 @@ struct DmaCols {
 };
 
 // Dynamic LDS of a kernel: SA stages of the A tile and SB of the B tile,
-// or, after the main loop, the epilogue's staging area (WTM x (BN + 4) fp32)
-// plus EXTRA bytes, whichever is larger.
+// or, after the main loop, the epilogue's staging area (EPI_ROWS x (BN + 4)
+// fp32) plus EXTRA bytes, whichever is larger.
 template <class C, class OA, class OB, int SA, int SB, size_t EXTRA = 0>
 struct Smem {
   static_assert(SA >= 2 && SB >= 2, "at least two stages per operand");
   static constexpr size_t B_OFS = (size_t)SA * OA::TILE_BYTES;
   static constexpr size_t OPERANDS = B_OFS + (size_t)SB * OB::TILE_BYTES;
-  static constexpr size_t EPI = (size_t)C::WTM * (C::BN + 4) * sizeof(float);
+  static constexpr size_t EPI = (size_t)C::EPI_ROWS * (C::BN + 4) * sizeof(float);
   static constexpr size_t EPI_ALL = EPI + EXTRA;
   static constexpr size_t BYTES = OPERANDS > EPI_ALL ? OPERANDS : EPI_ALL;
   static_assert(BYTES * C::WGS <= 160 * 1024, "gfx950 LDS per CU");
@@ -490,11 +496,11 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::FM][C::FN]) {
 }
 
 // Epilogue through LDS.  After the main loop the operand buffers are free;
-// the accumulators of one row of waves (WTM x BN fp32) are written there in
-// fully unrolled code (32x32 MFMA output layout: element r of a lane sits at
-// column lane % 32, row 8*(r/4) + 4*(lane/32) + r%4 of its 32x32 tile), then
-// every thread walks 8-column pieces of those rows: fn(block_row, block_col,
-// v[8]).  Consecutive lanes take consecutive pieces
+// each pass writes the accumulators of EPI_WROWS rows of waves (EPI_ROWS x BN
+// fp32) there in fully unrolled code (32x32 MFMA output layout: element r of
+// a lane sits at column lane % 32, row 8*(r/4) + 4*(lane/32) + r%4 of its
+// 32x32 tile), then every thread walks 8-column pieces of those rows:
+// fn(block_row, block_col, v[8]).  Consecutive lanes take consecutive pieces
 // of a row, so 8 aligned lanes cover one 64-column block and global accesses
 // are 16-byte vectors.  Every lane of every wave runs the same number of
 // pieces, so fn may use cross-lane operations within groups of 8 lanes.
@@ -502,24 +508,28 @@ template <class C>
 struct Stage {
   static constexpr int LS = C::BN + 4;  // staged row stride in floats (16-byte pad)
   static constexpr int SUBS = C::BN / 8;
-  static constexpr size_t BYTES = (size_t)C::WTM * LS * sizeof(float);
-  static_assert((C::WTM * SUBS) % C::NT == 0, "uniform piece count per lane");
+  static constexpr int WR = C::EPI_WROWS, ROWS = C::EPI_ROWS, PASSES = C::WAVES_M / WR;
+  static constexpr int NQ = ROWS * SUBS / C::NT;  // pieces per thread per pass
+  static_assert(C::WAVES_M % WR == 0, "whole passes");
+  static_assert((ROWS * SUBS) % C::NT == 0, "uniform piece count per lane");
 };
 
 template <class C, class Fn>
 __device__ __forceinline__ void staged_epilogue(float* stage, const f32x16_t (&acc)[C::FM][C::FN],
                                                 int wm, int wn, int lane, int tid, Fn fn) {
-  constexpr int LS = Stage<C>::LS, SUBS = Stage<C>::SUBS;
-  for (int p = 0; p < C::WAVES_M; ++p) {
+  typedef Stage<C> ST;
+  constexpr int LS = ST::LS, SUBS = ST::SUBS;
+  for (int p = 0; p < ST::PASSES; ++p) {
     __syncthreads();
-    if (wm == p) {
+    if (wm / ST::WR == p) {
+      const int r0 = (wm % ST::WR) * C::WTM;
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int row = r0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
             const int col = wn * C::WTN + j * 32 + (lane & 31);
             stage[row * LS + col] = acc[i][j][r];
           }
@@ -527,7 +537,7 @@ __device__ __forceinline__ void staged_epilogue(float* stage, const f32x16_t (&a
     __syncthreads();
     // Fully unrolled, so that the pieces' cross-lane reductions and stores
     // overlap instead of running as one dependent chain per piece.
-    constexpr int NQ = C::WTM * SUBS / C::NT;
+    constexpr int NQ = ST::NQ;
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int q = tid + i * C::NT;
@@ -535,7 +545,7 @@ __device__ __forceinline__ void staged_epilogue(float* stage, const f32x16_t (&a
       const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8);
       const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8 + 4);
       float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      fn(p * C::WTM + lrow, piece * 8, v);
+      fn(p * ST::ROWS + lrow, piece * 8, v);
     }
   }
 }
@@ -885,15 +895,15 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
                                             int wm, int wn, int lane, int tid, void* dW,
                                             int64_t m0, int n0, int64_t V, int H, float sc,
                                             bool accumulate) {
-  constexpr int LS = Stage<C>::LS, SUBS = Stage<C>::SUBS;
-  constexpr int NQ = C::WTM * SUBS / C::NT;  // pieces per thread per pass
+  typedef Stage<C> ST;
+  constexpr int LS = ST::LS, SUBS = ST::SUBS, NQ = ST::NQ;
   constexpr bool F32 = std::is_same<D, float>::value;
-  for (int p = 0; p < C::WAVES_M; ++p) {
+  for (int p = 0; p < ST::PASSES; ++p) {
     u32x4_t old[NQ][F32 ? 2 : 1];
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int q = tid + i * C::NT, lrow = q / SUBS, piece = q % SUBS;
-      const int64_t gm = m0 + p * C::WTM + lrow;
+      const int64_t gm = m0 + p * ST::ROWS + lrow;
       const int gn = n0 + piece * 8;
       const bool live = accumulate && gm < V && gn < H;
 #pragma unroll
@@ -908,14 +918,15 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
       }
     }
     __syncthreads();
-    if (wm == p) {
+    if (wm / ST::WR == p) {
+      const int r0 = (wm % ST::WR) * C::WTM;
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int row = r0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
             const int col = wn * C::WTN + j * 32 + (lane & 31);
             stage[row * LS + col] = acc[i][j][r];
           }
@@ -924,7 +935,7 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int q = tid + i * C::NT, lrow = q / SUBS, piece = q % SUBS;
-      const int64_t gm = m0 + p * C::WTM + lrow;
+      const int64_t gm = m0 + p * ST::ROWS + lrow;
       const int gn = n0 + piece * 8;
       if (gm >= V || gn >= H) continue;
       const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8);
