@@ -1,4 +1,5 @@
-"""Nothing is written outside the caller's buffers.
+"""Nothing is written outside the caller's output buffers, and the inputs are
+left untouched.
 
 The loss, dX, dW and the workspace are each carved out of a larger device
 buffer whose bytes before and after the region hold a fixed pattern; after a
@@ -79,6 +80,8 @@ def test_writes_stay_inside_buffers(pkg, case):
                           torch.cuda.current_stream(dev).cuda_stream, st)
     torch.cuda.synchronize()
     assert rc == 0, pkg.flce_status_string(rc)
+    # inputs are read only
+    assert torch.equal(Xd.cpu(), X) and torch.equal(Wd.cpu(), W) and torch.equal(td.cpu(), t)
     for name, b in (("loss", loss), ("dX", dX), ("dW", dW), ("workspace", ws)):
         if b is not None:
             assert b.intact(), f"{name} guard bytes overwritten"
