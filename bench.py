@@ -81,6 +81,10 @@ def parse():
                    help="comma-separated chunk sizes (0: the MI355X default policy): time the "
                         "workload at each and print one JSON line with the curve, then exit")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--autograd", action="store_true",
+                   help="time the differentiable path instead (forward + loss.backward() "
+                        "through fused_linear_cross_entropy, weight-dtype dW) and print "
+                        "one {\"autograd\": ...} line")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run plain 1 GiB device copies (reference for HBM byte counters)")
     p.add_argument("--record-traffic", nargs=4, metavar=("KERNEL", "WORKLOAD", "FETCH_CSV",
@@ -359,6 +363,65 @@ def recorded_traffic(kernel: str, workload: str):
     return float(kv["hbm_bytes_per_launch"])
 
 
+def autograd_bench(a, cfg, dev):
+    """The differentiable path: loss = fused_linear_cross_entropy(...);
+    loss.backward(), with dW accumulated in fp32 and returned in the weight dtype
+    (the wrapper tail: the fp32 -> weight-dtype cast and the upstream scaling)."""
+    import torch
+    import linear_cross_entropy_chunked_amd as pkg
+    host, (X, W, t) = make_inputs(cfg, dev)
+    x = X.clone().requires_grad_(True)
+    w = W.clone().requires_grad_(cfg.get("frozen", False) is False)
+    accum = torch.float32 if cfg["accum"] == "f32" else None
+
+    def step():
+        x.grad = None
+        w.grad = None
+        loss = pkg.fused_linear_cross_entropy(x, w, t, reduction=cfg["reduction"],
+                                              chunk_size=cfg["chunk"] or None,
+                                              accum_dtype=accum)
+        loss.backward()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    pkg.flce_profile_begin()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / a.steps * 1e3
+    prof = pkg.flce_profile_end()
+    wdt = w.grad.dtype if w.grad is not None else None
+    # (backward runs on autograd's device thread, outside this thread's profile window)
+    kernels = {k: dict(launches=v[0] // a.steps, ms_per_step=v[1] / a.steps)
+               for k, v in prof.items() if v[0]}
+    # the wrapper tail alone: the same scale/cast calls on tensors of the same sizes
+    tail_ms = None
+    if w.grad is not None and accum is not None and w.dtype != torch.float32:
+        dw32 = torch.empty(w.shape, dtype=torch.float32, device=dev).normal_()
+        dx = torch.empty_like(x)
+        g = torch.ones(1, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for rep in range(3):
+            e0.record()
+            pkg.scale_cast(dw32, w.dtype, scale=g)
+            pkg.scale_cast(dx, dx.dtype, scale=g, out=dx)
+            e1.record()
+            torch.cuda.synchronize()
+            tail_ms = e0.elapsed_time(e1)
+        del dw32, dx
+    x.grad = None
+    w.grad = None
+    raw, _ = run_workload(a.workload, cfg, a.steps, a.warmup, dev, host_dev=(host, (X, W, t)))
+    print(json.dumps({"autograd": {"workload": a.workload, "ms_per_step": ms,
+                                   "tokens_per_s": cfg["BT"] / (ms * 1e-3),
+                                   "raw_call_ms_per_step": raw["ms_per_step"],
+                                   "wrapper_tail_ms": tail_ms,
+                                   "weight_grad_dtype": str(wdt) if wdt is not None else None,
+                                   "forward_kernels": kernels}}), flush=True)
+
+
 def chunk_sweep(a, cfg, dev):
     """Time one workload at several chunk sizes (same inputs); 0 = the MI355X policy."""
     import linear_cross_entropy_chunked_amd as pkg
@@ -407,6 +470,9 @@ def main():
     cfg = WORKLOADS[a.workload]
     if a.chunk_sweep:
         chunk_sweep(a, cfg, dev)
+        return
+    if a.autograd:
+        autograd_bench(a, cfg, dev)
         return
     main_res, host = run_workload(a.workload, cfg, a.steps, a.warmup, dev)
     extras = {}

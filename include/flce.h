@@ -239,13 +239,15 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
                     const flce_options_t* opt);
 
 /*
- * dst[i] = scale * src[i], converted to dst_dtype (round to nearest even).
- * Serves the wrapper's two elementwise steps: the final cast of an fp32
- * grad_weight to the weight dtype (PR #1554, Tests: chunk storage is released
- * before the final cast) and scaling the stored gradients by the upstream
- * gradient in backward.  src [n] src_dtype, dst [n] dst_dtype, device
- * pointers, 16-byte aligned; scale is a device float (NULL = 1).  src == dst
- * is allowed when the dtypes match.  Enqueued on `stream`.
+ * dst[i] = scale * src[i], converted to dst_dtype: the product is rounded to
+ * fp32, then to dst_dtype (round to nearest even).  Serves the wrapper's two
+ * elementwise steps: the final cast of an fp32 grad_weight to the weight
+ * dtype (PR #1554, Tests: chunk storage is released before the final cast)
+ * and scaling the stored gradients by the upstream gradient in backward.
+ * src [n] src_dtype, dst [n] dst_dtype, device pointers of any alignment
+ * (16-byte-aligned ones are moved as 16-byte vectors); scale is a device
+ * float (NULL = 1).  src == dst is allowed when the dtypes match; n = 0 does
+ * nothing.  Enqueued on `stream`.
  */
 int flce_scale_cast(const void* src, flce_dtype_t src_dtype, void* dst, flce_dtype_t dst_dtype,
                     int64_t n, const float* scale, void* stream);

@@ -310,7 +310,7 @@ int flce_scale_cast(const void* src, flce_dtype_t src_dtype, void* dst, flce_dty
   if (n < 0 || (n > 0 && (!src || !dst))) return FLCE_E_ARG;
   if (src_dtype < FLCE_F32 || src_dtype > FLCE_BF16) return FLCE_E_DTYPE;
   if (dst_dtype < FLCE_F32 || dst_dtype > FLCE_BF16) return FLCE_E_DTYPE;
-  if (src == dst && src_dtype != dst_dtype) return FLCE_E_ARG;
+  if (n > 0 && src == dst && src_dtype != dst_dtype) return FLCE_E_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   FLCE_LAUNCH(FLCE_K_FILL, launch_scale_cast(src, (int)src_dtype, dst, (int)dst_dtype, n, scale,
                                              st));
