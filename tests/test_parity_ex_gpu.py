@@ -212,3 +212,43 @@ def test_mi355x_policy_is_an_explicit_chunk(pkg):
     torch.cuda.synchronize()
     assert a.stats["chunk_size"] == c
     assert torch.equal(a.loss, b.loss) and torch.equal(a.dX, b.dX) and torch.equal(a.dW, b.dW)
+
+
+def test_full_size_llama_bias_zloss_outputs(pkg):
+    """The optional parts at the Llama-3-8B lm_head shape (bf16, BT 8192,
+    H 4096, V 128256, chunk 2048, reduction none, 5 % of rows ignored): the
+    loss, z-loss, predicted token and accuracy of sampled rows (three labelled,
+    one ignored) against the oracle's forward run on those rows alone; with
+    reduction none each of these depends on its own row only.  (The oracle's
+    loops take about ten seconds for four rows at this size; the gradients
+    with bias and z-loss are compared in full at the smaller sizes above.)"""
+    BT, H, V, seed = 8192, 4096, 128256, 1001
+    X = si.make_x(BT, H, "bf16", seed)
+    W = si.make_w(V, H, "bf16", seed)
+    t = si.make_targets(BT, V, seed, ignore="scattered", frac=0.05)
+    b = (si.make_x(1, V, "f32", seed + 7).reshape(-1) * 0.5).to(torch.bfloat16)
+    lam = 1e-4
+    dev = torch.device("cuda:0")
+    r = pkg.fused_linear_cross_entropy_fwd_bwd(
+        X.to(dev), W.to(dev), t.to(dev), bias=b.to(dev), reduction="none", chunk_size=2048,
+        accum_dtype=torch.float32, z_loss_scale=lam, forward_only=True, return_z_loss=True,
+        return_accuracy=True, return_predicted=True)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(11))
+    lab_all = (t != -100).numpy()
+    rows = np.sort(np.concatenate([rng.choice(np.nonzero(lab_all)[0], 3, replace=False),
+                                   np.nonzero(~lab_all)[0][:1]]))
+    tr = t[rows]
+    ref = oracle.flce_ex(X[rows], W, tr, bias=b, z_loss_scale=lam, reduction="none",
+                         grads=False)
+    lab = (tr != -100).numpy()
+    loss = r.loss.cpu().numpy()[rows]
+    zl = r.z_loss.cpu().numpy()[rows]
+    assert np.all(loss[~lab] == 0.0) and np.all(zl[~lab] == 0.0)
+    assert _rel(loss[lab], ref["loss"][lab]) <= 2e-3
+    assert _rel(zl[lab], ref["z_loss"][lab]) <= 2e-3
+    pred = r.predicted.cpu().numpy()[rows]
+    Xd, Wd, bd = oracle.widen(X[rows]), oracle.widen(W), oracle.widen(b)
+    _check_predicted(pred, ref["predicted"], Xd, Wd, bd, tr.numpy())
+    acc = r.accuracy.cpu().numpy()[rows]
+    np.testing.assert_array_equal(acc, np.where(lab, (pred == tr.numpy()).astype(np.float64), 0.0))
