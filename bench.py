@@ -81,6 +81,9 @@ def parse():
                    help="comma-separated chunk sizes (0: the MI355X default policy): time the "
                         "workload at each and print one JSON line with the curve, then exit")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sensor-seconds", type=float, default=1.5,
+                   help="after each workload's timed steps, run it untimed this long while "
+                        "reading the GPU's clock, temperature and power (0: skip)")
     p.add_argument("--autograd", action="store_true",
                    help="time the differentiable path instead (forward + loss.backward() "
                         "through fused_linear_cross_entropy, weight-dtype dW) and print "
@@ -120,7 +123,7 @@ def make_inputs(cfg, dev):
     return host, (X.to(dev), W.to(dev), t.to(dev))
 
 
-def run_workload(name, cfg, steps, warmup, dev, host_dev=None):
+def run_workload(name, cfg, steps, warmup, dev, host_dev=None, sensor_s=0.0):
     import torch
     import linear_cross_entropy_chunked_amd as pkg
     import synthetic_inputs as si
@@ -171,6 +174,17 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None):
     step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     pct = lambda q: step_ms[min(len(step_ms) - 1, int(round(q * (len(step_ms) - 1))))]
     prof = pkg.flce_profile_end()
+    sensors = None
+    if sensor_s > 0:
+        # untimed: the same steps for about sensor_s seconds while the sampler reads the chip
+        s = GpuSensors(dev.index or 0).start()
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < sensor_s:
+            step()
+        torch.cuda.synchronize()
+        sensors = s.stop()
+        sensors["window"] = (f"untimed steps of the same workload for {sensor_s:.1f} s right "
+                             f"after the timed region")
     peak_transient = torch.cuda.max_memory_allocated(dev) - mem0
     del ws
     n_lab = st.n_valid
@@ -188,6 +202,7 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None):
         kernels={k: dict(launches=v[0] // steps, ms_per_launch=(v[1] / v[0] if v[0] else 0.0),
                          ms_per_step=v[1] / steps)
                  for k, v in prof.items() if v[0]},
+        gpu_sensors=sensors,
     )
     return res, host
 
@@ -231,6 +246,92 @@ def cpu_baseline(host, cfg, rows):
                        f"loop oracle (forward + backward, full H={cfg['H']}, V={cfg['V']}); "
                        f"{dt:.1f} s; widening the inputs to fp64 is not timed; host: "
                        f"{host_description()}")
+
+
+class GpuSensors:
+    """Shader clock, hotspot temperature and socket power of one GPU, read through the
+    ROCm SMI library (amdsmi) every `interval` s from a background thread.
+
+    Used over an untimed run of the same steps right after the timed region, so that
+    the readings describe the chip under the measured load without touching the timed
+    numbers.  Anything the platform does not expose is reported as unreadable."""
+
+    def __init__(self, torch_index=0, interval=0.05):
+        import threading
+        self.interval, self.idx = interval, torch_index
+        self.samples, self.error = [], None
+        self._stop, self._ready = threading.Event(), threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _handle(self, amdsmi):
+        import torch
+        handles = amdsmi.amdsmi_get_processor_handles()
+        p = torch.cuda.get_device_properties(self.idx)
+        bus = getattr(p, "pci_bus_id", None)
+        if bus is not None:
+            want = f"{getattr(p, 'pci_domain_id', 0):04x}:{bus:02x}:{getattr(p, 'pci_device_id', 0):02x}"
+            for h in handles:
+                if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(want):
+                    return h
+        if len(handles) == 1:
+            return handles[0]
+        raise RuntimeError(f"cannot match device {self.idx} among {len(handles)} SMI handles")
+
+    def _read(self, amdsmi, h):
+        def num(v):
+            return float(v) if isinstance(v, (int, float)) else None
+        clk = num(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("clk"))
+        temp = None
+        for kind in ("HOTSPOT", "JUNCTION", "EDGE"):
+            t = getattr(amdsmi.AmdSmiTemperatureType, kind, None)
+            if t is None:
+                continue
+            try:
+                temp = num(amdsmi.amdsmi_get_temp_metric(
+                    h, t, amdsmi.AmdSmiTemperatureMetric.CURRENT))
+            except Exception:
+                temp = None
+            if temp is not None:
+                break
+        pw = amdsmi.amdsmi_get_power_info(h)
+        power = next((num(pw.get(k)) for k in ("current_socket_power", "average_socket_power",
+                                                 "socket_power") if num(pw.get(k))), None)
+        return clk, temp, power
+
+    def _run(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            h = self._handle(amdsmi)
+            while True:
+                self.samples.append(self._read(amdsmi, h))
+                self._ready.set()
+                if self._stop.wait(self.interval):
+                    break
+        except Exception as e:  # no SMI access: report it, never fail the bench
+            self.error = f"{type(e).__name__}: {e}"
+        finally:
+            self._ready.set()
+
+    def start(self):
+        self._thread.start()
+        self._ready.wait(10.0)
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._thread.ident is not None:
+            self._thread.join(5.0)
+        if not self.samples:
+            return dict(readable=False, reason=self.error or "no sample within 10 s")
+
+        def spread(i):
+            v = sorted(s[i] for s in self.samples if s[i] is not None)
+            return [v[0], v[len(v) // 2], v[-1]] if v else None
+        return dict(readable=True, samples=len(self.samples),
+                    gfx_clock_mhz_min_median_max=spread(0),
+                    hotspot_temp_c_min_median_max=spread(1),
+                    socket_power_w_min_median_max=spread(2), error=self.error)
 
 
 def host_description() -> str:
@@ -474,7 +575,8 @@ def main():
     if a.autograd:
         autograd_bench(a, cfg, dev)
         return
-    main_res, host = run_workload(a.workload, cfg, a.steps, a.warmup, dev)
+    main_res, host = run_workload(a.workload, cfg, a.steps, a.warmup, dev,
+                                  sensor_s=a.sensor_seconds)
     extras = {}
     for name in [e for e in a.extra.split(",") if e and e != a.workload]:
         ecfg = WORKLOADS[name]
@@ -483,9 +585,18 @@ def main():
         if same:
             X, W, t = host
             hd = (host, (X.to(dev), W.to(dev), t.to(dev)))
-        extras[name], _ = run_workload(name, ecfg, max(a.steps // 2, 2), a.warmup, dev, hd)
+        extras[name], _ = run_workload(name, ecfg, max(a.steps // 2, 2), a.warmup, dev, hd,
+                                       sensor_s=a.sensor_seconds)
     rl = roofline(main_res, cfg)
     rl["traffic"] = recorded_traffic(rl["kernel"], a.workload)
+    sens = main_res["gpu_sensors"]
+    if rl["bound"] == "mfma" and sens and sens.get("readable") and \
+            sens["gfx_clock_mhz_min_median_max"]:
+        # the published peak assumes 2.4 GHz; the same fraction at the clock the chip held
+        mhz = sens["gfx_clock_mhz_min_median_max"][1]
+        if mhz:
+            rl["frac_at_measured_clock"] = rl["frac"] * 2400.0 / mhz
+            rl["measured_clock_mhz"] = mhz
     out = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],
