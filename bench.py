@@ -11,7 +11,9 @@ when the timed region starts.
 Prints one JSON line.  ``value`` = tokens/s of the whole job (BT x steps /
 elapsed).  ``roofline`` is for the dominant kernel, with its average launch
 duration measured by HIP events on the stream it runs on, over the timed
-steps.  ``cpu_baseline`` times the fp64 oracle on a bounded sample of rows of
+steps; only that kernel is bracketed by events there, and the per-kernel
+table in ``detail`` comes from further steps with every kernel bracketed.
+``cpu_baseline`` times the fp64 oracle on a bounded sample of rows of
 the same workload on the host cores.
 """
 from __future__ import annotations
@@ -157,13 +159,22 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None, sensor_s=0.0):
             raise pkg.FlceError(rc, "flce_fwd_bwd")
 
     log(f"{name}: {warmup} warmup step(s)")
+    # The warmup is profiled to find the kernel that dominates a step.  The timed
+    # steps then bracket only that kernel with HIP events (each pair of events
+    # adds a few microseconds to the stream; bracketing every kernel cost 0.6 %
+    # of a chunk-2048 step and 2.6 % of a chunk-256 one), and a second run of
+    # the same steps right after brackets every kernel for the per-kernel table.
+    pkg.flce_profile_begin()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log(f"{name}: {steps} timed step(s)")
+    wprof = pkg.flce_profile_end()
+    dominant = max(wprof, key=lambda k: wprof[k][1]) if any(v[0] for v in wprof.values()) \
+        else "dw_gemm"
+    log(f"{name}: {steps} timed step(s), events around {dominant}")
     # per-step HIP events on the library's stream, for the step-time spread
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    pkg.flce_profile_begin()
+    pkg.flce_profile_begin_kinds([dominant])
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(steps):
@@ -173,6 +184,14 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None, sensor_s=0.0):
     elapsed = time.perf_counter() - t0
     step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     pct = lambda q: step_ms[min(len(step_ms) - 1, int(round(q * (len(step_ms) - 1))))]
+    tprof = pkg.flce_profile_end()[dominant]
+    log(f"{name}: {steps} step(s) with every kernel bracketed")
+    pkg.flce_profile_begin()
+    t1 = time.perf_counter()
+    for i in range(steps):
+        step()
+    torch.cuda.synchronize()
+    profiled_ms = (time.perf_counter() - t1) / steps * 1e3
     prof = pkg.flce_profile_end()
     sensors = None
     if sensor_s > 0:
@@ -199,18 +218,24 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None, sensor_s=0.0):
         algorithmic_tflops=flops / (ms * 1e-3) / 1e12,
         mfma_frac=flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[cfg["dtype"]],
         workspace_bytes=wsb, peak_transient_bytes=int(peak_transient),
+        timed_kernel=dict(name=dominant, launches=tprof[0] // steps,
+                          ms_per_launch=(tprof[1] / tprof[0] if tprof[0] else 0.0),
+                          ms_per_step=tprof[1] / steps),
         kernels={k: dict(launches=v[0] // steps, ms_per_launch=(v[1] / v[0] if v[0] else 0.0),
                          ms_per_step=v[1] / steps)
                  for k, v in prof.items() if v[0]},
+        kernels_pass=(f"{steps} further steps with every kernel bracketed by HIP events "
+                      f"({profiled_ms:.3f} ms per step)"),
         gpu_sensors=sensors,
     )
     return res, host
 
 
 def roofline(res, cfg):
-    """Roofline figures of the dominant kernel of one step."""
+    """Roofline figures of the dominant kernel of one step, timed in the timed steps."""
     c, H, V = res["chunk_size"], res["H"], res["V"]
-    name, k = max(res["kernels"].items(), key=lambda kv: kv[1]["ms_per_step"])
+    k = res["timed_kernel"]
+    name = k["name"]
     s = 4 if cfg["dtype"] == "f32" else 2
     if name in ("logits_gemm", "dx_gemm", "dw_gemm"):
         # per launch: one full chunk of c rows -> 2 c H V flops
@@ -486,12 +511,16 @@ def autograd_bench(a, cfg, dev):
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    pkg.flce_profile_begin()
     t0 = time.perf_counter()
     for _ in range(a.steps):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / a.steps * 1e3
+    # the per-kernel table from further steps (the events are kept out of the timed ones)
+    pkg.flce_profile_begin()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
     prof = pkg.flce_profile_end()
     wdt = w.grad.dtype if w.grad is not None else None
     # (backward runs on autograd's device thread, outside this thread's profile window)

@@ -288,6 +288,12 @@ typedef struct {
 /* Open a profile on the calling thread (clears any previous one). */
 int flce_profile_begin(void);
 
+/* The same, bracketing only the kernels whose kind k has bit (1u << k) set
+ * in kind_mask: each pair of events adds a few microseconds to the stream,
+ * so a timed run brackets only the kernel it measures.  FLCE_E_ARG (and no
+ * change) for an empty mask or bits at or above FLCE_K_COUNT. */
+int flce_profile_begin_kinds(uint32_t kind_mask);
+
 /* Close it: waits for the recorded events and fills *out.  Returns
  * FLCE_E_ARG if no profile is open. */
 int flce_profile_end(flce_profile_t* out);

@@ -28,7 +28,8 @@ KERNEL_KINDS = ["mask_scan", "zero_ignored_rows", "logits_gemm", "softmax_grad",
 # Every symbol include/flce.h declares.
 EXPORTS = ["flce_chunk_size", "flce_chunk_size_mi355x", "flce_workspace_bytes", "flce_fwd_bwd", "flce_workspace_bytes_ex",
            "flce_fwd_bwd_ex", "flce_scale_cast", "flce_status_string", "flce_last_error",
-           "flce_profile_begin", "flce_profile_end", "flce_kernel_name"]
+           "flce_profile_begin", "flce_profile_begin_kinds", "flce_profile_end",
+           "flce_kernel_name"]
 
 
 class FlceError(RuntimeError):
@@ -98,6 +99,8 @@ def load():
     lib.flce_last_error.restype = ctypes.c_char_p
     lib.flce_profile_begin.argtypes = []
     lib.flce_profile_begin.restype = I
+    lib.flce_profile_begin_kinds.argtypes = [ctypes.c_uint32]
+    lib.flce_profile_begin_kinds.restype = I
     lib.flce_profile_end.argtypes = [ctypes.POINTER(FlceProfile)]
     lib.flce_profile_end.restype = I
     lib.flce_kernel_name.argtypes = [I]
@@ -168,6 +171,14 @@ def flce_last_error() -> str:
 
 def flce_profile_begin() -> int:
     return load().flce_profile_begin()
+
+
+def flce_profile_begin_kinds(kinds) -> int:
+    """Profile only the named kernel kinds (names from KERNEL_KINDS)."""
+    mask = 0
+    for k in kinds:
+        mask |= 1 << KERNEL_KINDS.index(k)
+    return load().flce_profile_begin_kinds(mask)
 
 
 def flce_profile_end() -> dict:

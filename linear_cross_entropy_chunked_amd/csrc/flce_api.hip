@@ -144,6 +144,7 @@ struct ProfRec {
 };
 struct Profiler {
   bool open = false;
+  uint32_t kinds = 0;  // bit k set: kernels of kind k are bracketed
   std::vector<ProfRec> recs;
   std::vector<hipEvent_t> pool;
   hipEvent_t get() {
@@ -164,7 +165,7 @@ struct ProfScope {
   bool on = false;
   ProfRec rec{};
   ProfScope(int kind, hipStream_t s) : st(s) {
-    if (!g_prof.open) return;
+    if (!g_prof.open || !((g_prof.kinds >> kind) & 1u)) return;
     rec.kind = kind;
     rec.a = g_prof.get();
     rec.b = g_prof.get();
@@ -271,15 +272,19 @@ const char* flce_kernel_name(int kind) {
   return (kind >= 0 && kind < FLCE_K_COUNT) ? names[kind] : "unknown";
 }
 
-int flce_profile_begin(void) {
+int flce_profile_begin_kinds(uint32_t kind_mask) {
+  if (kind_mask == 0 || (kind_mask >> FLCE_K_COUNT) != 0) return FLCE_E_ARG;
   for (auto& r : g_prof.recs) {
     g_prof.pool.push_back(r.a);
     g_prof.pool.push_back(r.b);
   }
   g_prof.recs.clear();
+  g_prof.kinds = kind_mask;
   g_prof.open = true;
   return FLCE_OK;
 }
+
+int flce_profile_begin(void) { return flce_profile_begin_kinds((1u << FLCE_K_COUNT) - 1u); }
 
 int flce_profile_end(flce_profile_t* out) {
   if (!g_prof.open) return FLCE_E_ARG;

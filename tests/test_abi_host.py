@@ -205,3 +205,18 @@ def test_policy_rejects_invalid_arguments(flce_lib):
     assert f(8, 0, 8, 2, 2, 0, 0) == -1
     assert f(8, 8, 8, 7, 7, 0, 0) == -1
     assert f(8, 8, 8, 2, 1, 0, 0) == -1  # bf16 operands with an fp16 accumulator
+
+
+def test_profile_kind_mask_is_checked(flce_lib):
+    """flce_profile_begin_kinds rejects an empty mask and unknown kinds; an open
+    profile with nothing launched closes with zero counts (no HIP call)."""
+    lib = flce_lib.load()
+    assert lib.flce_profile_begin_kinds(0) == -1  # FLCE_E_ARG
+    assert lib.flce_profile_begin_kinds(1 << len(flce_lib.KERNEL_KINDS)) == -1
+    assert flce_lib.flce_profile_begin_kinds(["dw_gemm", "logits_gemm"]) == 0
+    prof = flce_lib.flce_profile_end()
+    assert all(v == (0, 0.0) for v in prof.values())
+    assert flce_lib.flce_profile_begin() == 0
+    flce_lib.flce_profile_end()
+    with pytest.raises(flce_lib.FlceError):
+        flce_lib.flce_profile_end()  # none open
