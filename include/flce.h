@@ -161,8 +161,10 @@ size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype
  * host sync).  Everything after that is enqueued asynchronously on `stream`;
  * outputs are valid in stream order.  FLCE_E_TARGET is reported at that sync,
  * before any projection runs; outputs are then unspecified.  Outputs must not
- * alias inputs or the workspace.  Calls are reentrant given distinct
- * workspaces.
+ * alias inputs, the workspace or each other: a written buffer whose byte range
+ * (as sized above, the workspace by flce_workspace_bytes) overlaps another
+ * buffer of the call returns FLCE_E_ARG before any launch.  Calls are
+ * reentrant given distinct workspaces.
  */
 int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
                  int64_t V, flce_dtype_t dtype, int64_t ignore_index, flce_reduction_t reduction,

@@ -196,6 +196,17 @@ thread_local ScanFlags* g_host_flags = nullptr;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// A buffer's byte range as the call uses it (empty when absent).
+struct Span {
+  const void* p;
+  uint64_t n;
+};
+bool overlap(const Span& a, const Span& b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -361,6 +372,34 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
   const Extras ext = extras_of(&o);
   const Layout L = make_layout(BT, H, V, dtype, c, ext);
   if (!workspace || !aligned(workspace, kAlign)) return FLCE_E_ARG;
+  {
+    // Every buffer the call writes must be disjoint from every other buffer it
+    // reads or writes (the kernels read inputs while outputs are being written).
+    const bool none_red = reduction == FLCE_NONE;
+    const uint64_t s = itemsize(dtype), a = itemsize(accum_dtype);
+    const uint64_t per_tok = none_red ? 4ull * (uint64_t)BT : 4ull;
+    const Span written[] = {
+        {loss, per_tok},
+        {grads ? dX : nullptr, (uint64_t)BT * H * s},
+        {want_dw ? dW : nullptr, (uint64_t)V * H * a},
+        {workspace, L.total},
+        {grads ? o.grad_bias : nullptr, (uint64_t)V * a},
+        {o.z_loss, per_tok},
+        {o.accuracy, per_tok},
+        {o.predicted, 8ull * (uint64_t)BT}};
+    const Span read[] = {{X, (uint64_t)BT * H * s},
+                         {W, (uint64_t)V * H * s},
+                         {targets, 8ull * (uint64_t)BT},
+                         {grad_output, per_tok},
+                         {o.bias, (uint64_t)V * s}};
+    const int nw = (int)(sizeof written / sizeof written[0]);
+    for (int i = 0; i < nw; ++i) {
+      for (int j = i + 1; j < nw; ++j)
+        if (overlap(written[i], written[j])) return FLCE_E_ARG;
+      for (const Span& r : read)
+        if (overlap(written[i], r)) return FLCE_E_ARG;
+    }
+  }
   if (workspace_bytes < L.total) return FLCE_E_WORKSPACE;
 
   hipStream_t st = static_cast<hipStream_t>(stream);

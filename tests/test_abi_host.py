@@ -104,11 +104,18 @@ def test_workspace_invalid_arguments(flce_lib):
 
 
 # ------------------------------------------------ rejected before any launch
+# Fake, disjoint device addresses (never dereferenced: every call below fails
+# on the host before anything is enqueued).
+FAKE = dict(X=0x10000, W=0x20000, targets=0x30000, loss=0x40000, dX=0x50000, dW=0x60000,
+            workspace=0x70000)
+
+
 def _call(flce_lib, **kw):
-    a = dict(X=16, W=16, targets=16, BT=4, H=64, V=10, dtype=flce_lib.BF16, ignore_index=-100,
-             reduction=0, chunk_size=0, chunk_mem_const=1, accum_dtype=flce_lib.BF16,
-             frozen_weight=0, accumulate_dw=0, grad_output=None, loss=16, dX=16, dW=16,
-             workspace=256, workspace_bytes=1 << 30, stream=None)
+    a = dict(X=FAKE["X"], W=FAKE["W"], targets=FAKE["targets"], BT=4, H=64, V=10,
+             dtype=flce_lib.BF16, ignore_index=-100, reduction=0, chunk_size=0,
+             chunk_mem_const=1, accum_dtype=flce_lib.BF16, frozen_weight=0, accumulate_dw=0,
+             grad_output=None, loss=FAKE["loss"], dX=FAKE["dX"], dW=FAKE["dW"],
+             workspace=FAKE["workspace"], workspace_bytes=1 << 30, stream=None)
     a.update(kw)
     return flce_lib.flce_fwd_bwd(**a)
 
@@ -124,15 +131,35 @@ def _call(flce_lib, **kw):
     (dict(loss=None), -1),
     (dict(dW=None), -1),                       # trained weight needs dW
     (dict(X=None), -1),
-    (dict(X=18), -1),                          # misaligned
+    (dict(X=FAKE["X"] + 2), -1),               # misaligned
     (dict(workspace=None), -1),
-    (dict(workspace=272), -1),                 # workspace must be 256-byte aligned
+    (dict(workspace=FAKE["workspace"] + 16), -1),  # workspace must be 256-byte aligned
     (dict(workspace_bytes=1), -4),
     (dict(chunk_mem_const=0), -1),
     (dict(frozen_weight=2), -1),
 ])
 def test_invalid_arguments_rejected_on_host(flce_lib, kw, status):
     assert _call(flce_lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dX=FAKE["X"] + 256),                  # grad_input over the inputs
+    dict(dW=FAKE["W"]),                        # grad_weight onto the weight
+    dict(loss=FAKE["workspace"] + 64),         # loss inside the workspace
+    dict(loss=FAKE["targets"] + 16),           # loss over the targets
+    dict(dX=FAKE["dW"] + 512),                 # two outputs overlapping
+    dict(workspace=FAKE["dX"]),                # workspace over an output
+    dict(grad_output=FAKE["loss"], reduction=2),  # per-token upstream gradient over the loss
+])
+def test_overlapping_buffers_rejected_on_host(flce_lib, kw):
+    """A written buffer overlapping any other buffer of the call is refused
+    before any launch.  The workspace is declared too small as well, so that a
+    missed check would stop at the workspace check (FLCE_E_WORKSPACE) rather
+    than enqueue anything."""
+    assert _call(flce_lib, workspace_bytes=1) == -4  # the addresses alone are fine
+    assert _call(flce_lib, workspace_bytes=1, **kw) == -1
+    # frozen: dW is not written, so it may sit anywhere
+    assert _call(flce_lib, workspace_bytes=1, frozen_weight=1, dW=FAKE["W"]) == -4
 
 
 # ----------------------------------------------------------------- options
@@ -155,10 +182,12 @@ def test_invalid_options_rejected_on_host(flce_lib):
     anything is enqueued on the fake pointers."""
     O = flce_lib.FlceOptions
     ws = 1
-    base = dict(X=256, W=256, targets=256, BT=4, H=8, V=16, dtype=flce_lib.F32, ignore_index=-100,
-                reduction=flce_lib.MEAN, chunk_size=4, chunk_mem_const=1, accum_dtype=flce_lib.F32,
-                frozen_weight=0, accumulate_dw=0, grad_output=None, loss=256, dX=256, dW=256,
-                workspace=256, workspace_bytes=ws, stream=None)
+    base = dict(X=FAKE["X"], W=FAKE["W"], targets=FAKE["targets"], BT=4, H=8, V=16,
+                dtype=flce_lib.F32, ignore_index=-100, reduction=flce_lib.MEAN, chunk_size=4,
+                chunk_mem_const=1, accum_dtype=flce_lib.F32, frozen_weight=0, accumulate_dw=0,
+                grad_output=None, loss=FAKE["loss"], dX=FAKE["dX"], dW=FAKE["dW"],
+                workspace=FAKE["workspace"], workspace_bytes=ws, stream=None)
+    assert flce_lib.flce_fwd_bwd_ex(*base.values(), None, O()) == -4  # only the workspace is short
     for bad in (O(2), O(0, 8), O(0, None, 8), O(0, None, None, -1.0), O(0, None, None, float("nan")),
                 O(0, None, None, 0.0, None, None, 4)):
         rc = flce_lib.flce_fwd_bwd_ex(*base.values(), None, bad)
