@@ -83,6 +83,12 @@ def parse():
                    help="comma-separated chunk sizes (0: the MI355X default policy): time the "
                         "workload at each and print one JSON line with the curve, then exit")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--protocol", default="",
+                   help="comma-separated workloads, or 'all': time them together, one step "
+                        "each per round in a seeded random order (--steps rounds), with the "
+                        "peak transient memory of each in two isolated samples, print one "
+                        "{\"protocol\": ...} line and exit")
+    p.add_argument("--protocol-seed", type=int, default=1234)
     p.add_argument("--sensor-seconds", type=float, default=1.5,
                    help="after each workload's timed steps, run it untimed this long while "
                         "reading the GPU's clock, temperature and power (0: skip)")
@@ -125,7 +131,10 @@ def make_inputs(cfg, dev):
     return host, (X.to(dev), W.to(dev), t.to(dev))
 
 
-def run_workload(name, cfg, steps, warmup, dev, host_dev=None, sensor_s=0.0):
+def prepare(cfg, dev, host_dev=None):
+    """Inputs, outputs and the library call of one workload; the workspace is
+    passed to each call, so that its allocation can be measured."""
+    import types
     import torch
     import linear_cross_entropy_chunked_amd as pkg
     import synthetic_inputs as si
@@ -141,15 +150,11 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None, sensor_s=0.0):
             else None)
     dX = torch.empty_like(X)
     dW = None if frozen else torch.empty(V, H, dtype=tdt[adt], device=dev)
-    torch.cuda.synchronize()
-    mem0 = torch.cuda.memory_allocated(dev)
-    torch.cuda.reset_peak_memory_stats(dev)
     wsb = pkg.flce_workspace_bytes(BT, H, V, dt, cfg["chunk"], 1)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     st = pkg.FlceStats()
 
-    def step():
+    def call(ws):
         rc = pkg.flce_fwd_bwd(X.data_ptr(), W.data_ptr(), t.data_ptr(), BT, H, V, dt, -100, red,
                               cfg["chunk"], 1, adt, int(frozen), 0,
                               None if gout is None else gout.data_ptr(), loss.data_ptr(),
@@ -157,6 +162,24 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None, sensor_s=0.0):
                               wsb, stream.cuda_stream, st)
         if rc != 0:
             raise pkg.FlceError(rc, "flce_fwd_bwd")
+    return types.SimpleNamespace(host=host, call=call, wsb=wsb, st=st, stream=stream,
+                                 frozen=frozen, flops_per_row=(4 if frozen else 6) * H * V)
+
+
+def run_workload(name, cfg, steps, warmup, dev, host_dev=None, sensor_s=0.0):
+    import torch
+    import linear_cross_entropy_chunked_amd as pkg
+    BT, H, V = cfg["BT"], cfg["H"], cfg["V"]
+    p = prepare(cfg, dev, host_dev)
+    host, st, stream, frozen = p.host, p.st, p.stream, p.frozen
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    wsb = p.wsb
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def step():
+        p.call(ws)
 
     log(f"{name}: {warmup} warmup step(s)")
     # The warmup is profiled to find the kernel that dominates a step.  The timed
@@ -552,6 +575,79 @@ def autograd_bench(a, cfg, dev):
                                    "forward_kernels": kernels}}), flush=True)
 
 
+PROTOCOL_WORKLOADS = [
+    "llama3_8b_lm_head", "llama3_8b_lm_head_c256", "same_dtype_sweep_bf16",
+    "same_dtype_sweep_f16", "same_dtype_sweep_f32", "long_seq_8k_c256", "long_seq_32k_c256",
+    "long_seq_32k_default", "masked_sft_100_trained", "masked_sft_75_trained",
+    "masked_sft_50_trained", "masked_sft_10_trained", "masked_sft_100_frozen",
+    "masked_sft_10_frozen"]
+
+
+def protocol(a, dev):
+    """Every workload measured together: warmup steps for each, then rounds in
+    which the workloads run in a seeded random order, one step each, timed with
+    HIP events on the library's stream; the peak transient memory of each in two
+    isolated samples (a fresh workspace allocated inside the measured window)."""
+    import numpy as np
+    import torch
+    names = [n for n in a.protocol.split(",") if n] if a.protocol != "all" else PROTOCOL_WORKLOADS
+    hosts, preps = {}, {}
+    for n in names:
+        cfg = WORKLOADS[n]
+        key = tuple(cfg.get(k) for k in ("BT", "H", "V", "dtype", "seed", "share", "seq_len"))
+        if key not in hosts:
+            hosts[key] = make_inputs(cfg, dev)
+        preps[n] = prepare(cfg, dev, hosts[key])
+    wss = {n: torch.empty(p.wsb, dtype=torch.uint8, device=dev) for n, p in preps.items()}
+    for n in names:
+        for _ in range(a.warmup):
+            preps[n].call(wss[n])
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(a.protocol_seed))
+    samples = {n: [] for n in names}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    orders = []
+    for r in range(a.steps):
+        order = [names[i] for i in rng.permutation(len(names))]
+        orders.append(order)
+        for n in order:
+            p = preps[n]
+            e0.record(p.stream)
+            p.call(wss[n])
+            e1.record(p.stream)
+            e1.synchronize()
+            samples[n].append(e0.elapsed_time(e1))
+        log(f"protocol round {r + 1}/{a.steps} done")
+    del wss
+    out = {}
+    for n in names:
+        p, cfg = preps[n], WORKLOADS[n]
+        v = sorted(samples[n])
+        q = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
+        mem = []
+        for _ in range(2):
+            torch.cuda.synchronize()
+            m0 = torch.cuda.memory_allocated(dev)
+            torch.cuda.reset_peak_memory_stats(dev)
+            ws = torch.empty(p.wsb, dtype=torch.uint8, device=dev)
+            p.call(ws)
+            torch.cuda.synchronize()
+            mem.append(int(torch.cuda.max_memory_allocated(dev) - m0))
+            del ws
+        med = q(0.5)
+        flops = p.flops_per_row * p.st.n_valid
+        out[n] = dict(step_ms_p20_p50_p80=[q(0.2), med, q(0.8)],
+                      tokens_per_s_at_median=cfg["BT"] / (med * 1e-3),
+                      mfma_frac_at_median=flops / (med * 1e-3) / 1e12
+                      / MFMA_PEAK_TFLOPS[cfg["dtype"]],
+                      chunk_size=p.st.chunk_size, chunks_run=p.st.chunks_run,
+                      n_valid=p.st.n_valid, workspace_bytes=p.wsb,
+                      peak_transient_bytes_two_samples=mem)
+    print(json.dumps({"protocol": {"seed": a.protocol_seed, "warmup": a.warmup,
+                                   "rounds": a.steps, "first_orders": orders[:2],
+                                   "workloads": out}}), flush=True)
+
+
 def chunk_sweep(a, cfg, dev):
     """Time one workload at several chunk sizes (same inputs); 0 = the MI355X policy."""
     import linear_cross_entropy_chunked_amd as pkg
@@ -597,6 +693,9 @@ def main():
     if a.copy_calibration:
         log("copy calibration: 2 x 1 GiB device copies")
         copy_calibration(dev)
+    if a.protocol:
+        protocol(a, dev)
+        return
     cfg = WORKLOADS[a.workload]
     if a.chunk_sweep:
         chunk_sweep(a, cfg, dev)
