@@ -148,7 +148,8 @@ size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype
  *   accumulate_dw                     0: dW is overwritten; 1: dW += this call's gradient
  *   grad_output  float, device        NULL means 1.  mean/sum: [1]; none: [BT].
  *                                     Read only at labelled rows.
- *   loss         float, device        mean/sum: [1]; none: [BT] with ignored rows +0.0.
+ *   loss         float, device        mean/sum: [1]; none: [BT] with ignored rows +0.0
+ *                                     (NULL allowed only for none with BT = 0).
  *                                     Mean over zero labelled rows is 0.
  *   dX           [BT, H] dtype        ignored rows +0.0
  *   dW           [V, H] accum_dtype   see accumulate_dw

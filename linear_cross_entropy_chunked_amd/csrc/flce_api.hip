@@ -349,7 +349,8 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
     return FLCE_E_ARG;
   if (frozen_weight != 0 && frozen_weight != 1) return FLCE_E_ARG;
   if (accumulate_dw != 0 && accumulate_dw != 1) return FLCE_E_ARG;
-  if (!loss) return FLCE_E_ARG;
+  // (reduction none over zero rows has an empty loss vector, which may be NULL)
+  if (!loss && !(reduction == FLCE_NONE && BT == 0)) return FLCE_E_ARG;
   flce_options_t o;
   std::memset(&o, 0, sizeof o);
   if (opt) o = *opt;

@@ -54,7 +54,7 @@ def make_targets(BT: int, V: int, seed: int, *, ignore: str = "none", frac: floa
         perm = _rng(seed + 3).permutation(BT)
         t[perm[:n_ign]] = ignore_index
     elif ignore == "prompt_first":
-        L = seq_len or BT
+        L = seq_len or max(BT, 1)
         for s0 in range(0, BT, L):
             n = min(L, BT - s0)
             t[s0:s0 + int(round(frac * n))] = ignore_index

@@ -129,6 +129,7 @@ def _call(flce_lib, **kw):
     (dict(V=0), -1),
     (dict(BT=-1), -1),
     (dict(loss=None), -1),
+    (dict(loss=None, reduction=2), -1),        # none needs [BT] unless BT = 0
     (dict(dW=None), -1),                       # trained weight needs dW
     (dict(X=None), -1),
     (dict(X=FAKE["X"] + 2), -1),               # misaligned
@@ -249,3 +250,10 @@ def test_profile_kind_mask_is_checked(flce_lib):
     flce_lib.flce_profile_end()
     with pytest.raises(flce_lib.FlceError):
         flce_lib.flce_profile_end()  # none open
+
+
+def test_none_over_zero_rows_needs_no_loss_buffer(flce_lib):
+    """Reduction none over BT = 0 rows has an empty loss vector: a NULL loss is
+    accepted, and with a frozen weight nothing at all is enqueued."""
+    assert _call(flce_lib, BT=0, reduction=2, loss=None, frozen_weight=1, dW=None) == 0
+    assert _call(flce_lib, BT=0, reduction=0, loss=None, frozen_weight=1, dW=None) == -1
