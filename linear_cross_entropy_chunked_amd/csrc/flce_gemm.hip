@@ -713,7 +713,8 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
       (K + KT<T, C>::BK - 1) / KT<T, C>::BK, smem_raw, wm, wn, lane, acc);
 
   // Epilogue: add the bias (when given; PR #1554, Tests: bias on and off),
-  // store the logits, and per (row, 64-column block) the max and the sum of
+  // store the logits relative to their 64-column block maximum (z - max, in
+  // the slab dtype), and per (row, 64-column block) the max and the sum of
   // exp(z - max) in fp32, plus, when predictions are wanted, the first column
   // holding that max.  Both tile shapes reduce a 64-column block the same way
   // (8 lanes x 8 values), so a row's log-sum-exp does not depend on the
@@ -786,7 +787,15 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
       stats[(int64_t)gm * a.stats_ld + gn / 64] = float2{mx, se};
       if (a.amax) a.amax[(int64_t)gm * a.stats_ld + gn / 64] = am;
     }
-    if (a.store_slab) store8<T>(slab + (int64_t)gm * a.ldz + gn, v);
+    if (a.store_slab) {
+      // The slab keeps each logit minus its block maximum: the entries that
+      // dominate the softmax are then small numbers, whose rounding to the
+      // slab dtype is small in absolute terms whatever the logits' scale.
+      float d8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d8[e] = v[e] - mx;
+      store8<T>(slab + (int64_t)gm * a.ldz + gn, d8);
+    }
     const int64_t d = tgt_s[brow] - gn;  // target column within this piece, if any
     float zt = 0.f;
 #pragma unroll

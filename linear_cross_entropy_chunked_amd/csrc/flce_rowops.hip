@@ -172,7 +172,11 @@ hipError_t launch_zero_ignored(const int64_t* targets, int64_t BT, int64_t H,
 //          is the optional z-loss coefficient, 0 by default)
 //   G_v  = gamma * ((1 + 2 lam lse) exp(z_v - lse) - [v == t]),
 //          gamma = g_i for none, else 1
-// written over the logits in the operand dtype (round to nearest even); the
+// The slab holds z_v - M_b, with M_b the maximum of v's 64-column block (fp32
+// difference rounded to the slab dtype), so exp(z_v - lse) is taken as
+// exp((z_v - M_b) + (M_b - lse)): its rounding error grows with the distance
+// from the block maximum, not with the size of the logits.  G is
+// written over the slab in the operand dtype (round to nearest even); the
 // slab's padding columns [V, ldz) become 0.  The mean/sum scale g/N or g is
 // applied later, in fp32, by the gradient GEMMs: folding 1/N into a 16-bit
 // slab would flush small fp16 probabilities to zero.
@@ -268,12 +272,14 @@ __global__ __launch_bounds__(SM_T) void softmax_kernel(SoftmaxArgs a) {
   for (int64_t c = c_beg + (int64_t)tid * VE; c < c_end; c += (int64_t)SM_T * VE) {
     u32x4_t raw = *reinterpret_cast<const u32x4_t*>(z + c);
     S* e = reinterpret_cast<S*>(&raw);
+    // the slab holds z - (block maximum); the VE columns share one 64-column block
+    const float off = st[c >> 6].x - lse;
 #pragma unroll
     for (int q = 0; q < VE; ++q) {
       const int64_t col = c + q;
       float g = 0.f;
       if (col < a.V) {
-        const float p = __expf(T::to_f32(e[q]) - lse);
+        const float p = __expf(T::to_f32(e[q]) + off);
         g = col == tgt ? pscale * p - gamma : pscale * p;
       }
       e[q] = T::from_f32(g);

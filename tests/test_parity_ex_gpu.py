@@ -23,7 +23,7 @@ import synthetic_inputs as si
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-3, 2e-2)}
-TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+TD = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def _rel(a, b):
@@ -252,3 +252,31 @@ def test_full_size_llama_bias_zloss_outputs(pkg):
     _check_predicted(pred, ref["predicted"], Xd, Wd, bd, tr.numpy())
     acc = r.accuracy.cpu().numpy()[rows]
     np.testing.assert_array_equal(acc, np.where(lab, (pred == tr.numpy()).astype(np.float64), 0.0))
+
+
+@pytest.mark.parametrize("dtype,shift", [("bf16", 48.0), ("f16", 1000.0), ("f32", 48.0)])
+def test_constant_logit_shift_leaves_gradients(pkg, dtype, shift):
+    """Adding one constant to every logit (a constant bias) leaves the softmax,
+    and so the gradients, unchanged.  At |z| of 48 (bf16) or 1000 (fp16) a
+    logit rounded to the operand dtype is off by up to 0.125 / 0.25, which would
+    move exp(z - lse) by 13-28 %; the slab keeps z minus its block maximum
+    instead, so the gradients still meet the 16-bit tolerance.  The row
+    targets are the argmax of each row, so p_target is large and its gradient
+    1 - p_target small: the case most sensitive to that rounding."""
+    BT, H, V = 96, 64, 500
+    X = si.make_x(BT, H, dtype, 51)
+    W = si.make_w(V, H, dtype, 51, scale=0.6)
+    z = oracle.widen(X) @ oracle.widen(W).T
+    t = torch.from_numpy(z.argmax(axis=1).astype(np.int64))
+    b = torch.full((V,), shift, dtype=TD[dtype])
+    dev = torch.device("cuda:0")
+    r = pkg.fused_linear_cross_entropy_fwd_bwd(
+        X.to(dev), W.to(dev), t.to(dev), bias=b.to(dev), reduction="sum", chunk_size=32,
+        accum_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.flce_ex(X, W, t, bias=b, reduction="sum")
+    tl, tg = {"f32": (1e-5, 1e-4), "bf16": (2e-3, 2e-2), "f16": (2e-3, 2e-2)}[dtype]
+    assert abs(float(r.loss) - ref["loss"]) <= tl * abs(ref["loss"])
+    assert _rel(r.dX.double().cpu(), ref["dX"]) <= tg
+    assert _rel(r.dW.double().cpu(), ref["dW"]) <= tg
+    assert _rel(r.grad_bias.double().cpu(), ref["grad_bias"]) <= tg

@@ -217,10 +217,9 @@ def test_all_rows_ignored_and_empty_batch(pkg):
 def test_degenerate_shapes(pkg, dtype, shape):
     """Smallest legal sizes and block edges: one row, H = 8 (the minimum), V = 1,
     V one column past a 64-column statistics block, 257 rows (one past a
-    256-row tile), the heuristic chunk.  With V = 1 the loss is exactly 0 and,
-    for fp32, so are both gradients; 16-bit operands keep the logits in the
-    operand dtype, so their gradient exp(z - lse) - 1 is of the size of the
-    rounding of z, which the absolute check of _check bounds."""
+    256-row tile), the heuristic chunk.  With V = 1 the loss and both gradients
+    are exactly 0 for every dtype: the slab holds each logit minus its block
+    maximum, 0 here, so exp(0 + max - lse) - 1 = 0 exactly."""
     BT, H, V, chunk = shape
     X, W, t = si.make_case(BT, H, V, dtype, 2700 + BT + V)
     g = si.make_grad_output(t, "sum", 2700, scalar=1.25)
@@ -229,8 +228,7 @@ def test_degenerate_shapes(pkg, dtype, shape):
     ref = oracle.flce(X, W, t, reduction="sum", grad_output=g)
     if V == 1:
         assert float(r.loss) == 0.0 and ref["loss"] == 0.0
-        if dtype == "f32":
-            assert (r.dX == 0).all() and (r.dW == 0).all()
+        assert (r.dX == 0).all() and (r.dW == 0).all()
     _check(r, ref, dtype, "sum")
 
 
