@@ -138,7 +138,7 @@ size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype
  *   W            [V, H]  dtype        lm_head weight
  *   targets      [BT]    int64        class ids; rows equal to ignore_index are
  *                                     ignored (any int64 value, default -100)
- *   BT, H, V                          BT >= 0, H >= 8 and H % 8 == 0, V >= 1
+ *   BT, H, V                          BT >= 0, 8 <= H <= 2^20 and H % 8 == 0, V >= 1
  *   dtype                             FLCE_F32, FLCE_F16 or FLCE_BF16
  *   reduction                         FLCE_MEAN, FLCE_SUM or FLCE_NONE
  *   chunk_size, chunk_mem_const       see flce_chunk_size

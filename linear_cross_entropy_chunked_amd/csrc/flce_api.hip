@@ -344,8 +344,9 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
   if (dtype < FLCE_F32 || dtype > FLCE_BF16) return FLCE_E_DTYPE;
   if (accum_dtype != dtype && accum_dtype != FLCE_F32) return FLCE_E_DTYPE;
   if (reduction < FLCE_MEAN || reduction > FLCE_NONE) return FLCE_E_ARG;
+  // H <= 2^20 keeps a 256-row tile of dW (fp32) within one 32-bit buffer range
   if (BT < 0 || BT > 0x7ffffffe || V < 1 || V > 0x7ffffffe || H < 8 || H % 8 != 0 ||
-      H > 0x7ffffffe)
+      H > (1 << 20))
     return FLCE_E_ARG;
   if (frozen_weight != 0 && frozen_weight != 1) return FLCE_E_ARG;
   if (accumulate_dw != 0 && accumulate_dw != 1) return FLCE_E_ARG;

@@ -907,6 +907,16 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
   typedef Stage<C> ST;
   constexpr int LS = ST::LS, SUBS = ST::SUBS, NQ = ST::NQ;
   constexpr bool F32 = std::is_same<D, float>::value;
+  constexpr uint64_t ES = F32 ? 4 : 2;
+  // The destination values are read through a buffer descriptor over this
+  // tile's rows of dW: a piece outside the matrix (or every piece, when not
+  // accumulating) takes an offset past the range and reads zeros, so the loads
+  // need no branches and the compiler can wait for them one piece at a time.
+  // (The library limits H to 2^20, so a tile's rows span at most 1 GiB.)
+  const int64_t trows = V - m0 < C::BM ? V - m0 : C::BM;
+  const uint64_t span = (uint64_t)trows * (uint64_t)H * ES;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<unsigned char*>(dW) + (uint64_t)m0 * (uint64_t)H * ES, 0, (int)span, 0x00020000);
   for (int p = 0; p < ST::PASSES; ++p) {
     u32x4_t old[NQ][F32 ? 2 : 1];
 #pragma unroll
@@ -917,13 +927,11 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
       const bool live = accumulate && gm < V && gn < H;
 #pragma unroll
       for (int h = 0; h < (F32 ? 2 : 1); ++h) {
-        old[i][h] = u32x4_t{0u, 0u, 0u, 0u};
-        if (live) {
-          if constexpr (F32)
-            old[i][h] = reinterpret_cast<const u32x4_t*>(static_cast<float*>(dW) + gm * H + gn)[h];
-          else
-            old[i][h] = *reinterpret_cast<const u32x4_t*>(static_cast<u16*>(dW) + gm * H + gn);
-        }
+        const uint32_t off =
+            live ? (uint32_t)(((uint64_t)(p * ST::ROWS + lrow) * (uint64_t)H + (uint64_t)gn) * ES) +
+                       16u * (uint32_t)h
+                 : kOOB;
+        old[i][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
       }
     }
     __syncthreads();

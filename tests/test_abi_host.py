@@ -126,6 +126,7 @@ def _call(flce_lib, **kw):
     (dict(reduction=3), -1),
     (dict(H=60), -1),                          # H must be a multiple of 8
     (dict(H=0), -1),
+    (dict(H=(1 << 20) + 8), -1),               # at most 2^20 hidden units
     (dict(V=0), -1),
     (dict(BT=-1), -1),
     (dict(loss=None), -1),
