@@ -2,7 +2,8 @@
 
 Each case draws its own shape and options: operand dtype, BT (including 0
 and 1), H (a multiple of 8), V (including 1 and sizes that are ragged against
-every tile), chunk_size (heuristic, powers of two, values that floor to one),
+every tile), chunk_size (heuristic with C = 1, 2, 8 or 16, the MI355X policy,
+powers of two, values that floor to one),
 dW in fp32 or the operand dtype, mean / sum / none, a frozen weight, dW
 accumulation onto a random buffer, an ignored share from none to all rows
 (scattered or prompt-first), an ignore_index inside [0, V) as well as -100,
@@ -48,9 +49,16 @@ def draw(i):
     ignore_index = -100 if r.random() < 0.7 else int(r.integers(0, V))
     poison = bool(r.random() < 0.5)
     scalar = float(pick([1.0, 0.5, 3.0]))
+    # drawn last, so that the fields above keep their values: the heuristic's
+    # memory multiplier C, and the MI355X policy in place of the heuristic
+    policy = pick([None, None, "mi355x"])
+    mem_const = int(pick([1, 1, 2, 8, 16]))
+    if chunk is None and policy is not None:
+        chunk = policy
     return dict(dtype=dtype, BT=BT, H=H, V=V, chunk=chunk, accum=accum, reduction=reduction,
                 frozen=frozen, accumulate=accumulate, ignore=ignore, frac=frac,
-                ignore_index=ignore_index, poison=poison, scalar=scalar, seed=5000 + 17 * i)
+                ignore_index=ignore_index, poison=poison, scalar=scalar, mem_const=mem_const,
+                seed=5000 + 17 * i)
 
 
 @pytest.fixture(scope="module")
@@ -91,7 +99,8 @@ def test_random_configuration(pkg, i):
     dev = torch.device("cuda:0")
     r = pkg.fused_linear_cross_entropy_fwd_bwd(
         Xg.to(dev), W.to(dev), t.to(dev), ignore_index=ii, reduction=c["reduction"],
-        chunk_size=c["chunk"], accum_dtype=adt if c["accum"] == "f32" else None,
+        chunk_size=c["chunk"], chunk_mem_const=c["mem_const"],
+        accum_dtype=adt if c["accum"] == "f32" else None,
         frozen_weight=c["frozen"], grad_output=g.to(dev),
         dW=None if dW0 is None else dW0.clone().to(dev), accumulate_dw=c["accumulate"])
     torch.cuda.synchronize()
