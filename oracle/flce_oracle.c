@@ -16,9 +16,9 @@
  * across FP16, BF16, and FP32", Background and motivation (the loss is the
  * linear projection followed by cross-entropy; chunking only avoids holding
  * all logits at once); PR #1554 (ignored-row skipping), Summary (the three
- * projections logits, grad_input, grad_weight; rows whose target equals
- * ignore_index add nothing to the loss or the gradients) and Details item 1
- * (such rows get a zero grad_input row and zero per-token loss).
+ * projections logits, grad_input, grad_weight; an ignored row contributes
+ * zero to the loss and to every gradient) and Details item 1 (an ignored
+ * row's grad_input row and per-token loss are zero).
  *
  * Chunking, row compaction and direct accumulation only reorder this exact
  * arithmetic (PR #1554, Details item 4: results agree up to rounding order),
@@ -430,26 +430,34 @@ int oracle_flce_ex(const double* X, const double* W, const double* bias, const i
     if (acc) acc[0] = d > 0.0 ? sa / d : 0.0;
   }
 
-  /* grad_input = G W, grad_weight = G^T X, grad_bias = column sums of G;
-   * ignored rows of G are zero, so they add nothing. */
-  if (dX)
+  /* grad_input = G W, grad_weight = G^T X, grad_bias = column sums of G,
+   * each summed over the labelled rows only (ascending).  An ignored row is
+   * never read: its X row may hold NaN or Inf, and 0 * NaN is NaN, so a sum
+   * over every row would let it into dW (PR #1554, Tests: NaN in ignored rows
+   * must reach neither the loss nor the gradients).  Its dX row is +0.0. */
+  if (dX) {
     for (int64_t i = 0; i < BT; ++i)
+      for (int64_t k = 0; k < H; ++k) dX[i * H + k] = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const int64_t i = idx[n];
       for (int64_t k = 0; k < H; ++k) {
         double a = 0.0;
         for (int64_t v = 0; v < V; ++v) a += G[i * V + v] * W[v * H + k];
         dX[i * H + k] = a;
       }
+    }
+  }
   if (dW)
     for (int64_t v = 0; v < V; ++v)
       for (int64_t k = 0; k < H; ++k) {
         double a = 0.0;
-        for (int64_t i = 0; i < BT; ++i) a += G[i * V + v] * X[i * H + k];
+        for (int64_t n = 0; n < N; ++n) a += G[idx[n] * V + v] * X[idx[n] * H + k];
         dW[v * H + k] = accumulate ? dW[v * H + k] + a : a;
       }
   if (grad_bias)
     for (int64_t v = 0; v < V; ++v) {
       double a = 0.0;
-      for (int64_t i = 0; i < BT; ++i) a += G[i * V + v];
+      for (int64_t n = 0; n < N; ++n) a += G[idx[n] * V + v];
       grad_bias[v] = accumulate ? grad_bias[v] + a : a;
     }
   free(idx); free(G); free(z); free(lrow); free(zrow); free(arow);

@@ -10,7 +10,10 @@ per-token outputs.  Each is checked against something other than the oracle:
 * invariants: without a z-loss term the bias gradient sums to zero over the
   vocabulary; with no bias and lam = 0 the extended oracle equals the base one;
 * ignored rows: 0 loss, z-loss and accuracy, -1 predicted token (PR #1554,
-  Details item 1);
+  Details item 1), and NaN or Inf placed in ignored X rows (and NaN in the
+  per-token upstream gradient there) changes no output bit, with the bias on
+  and a z-loss coefficient (PR #1554, Tests: ignored rows never enter the
+  projection; the ignored-row cases run with bias on and off);
 * planted mistakes in the new code must fail these pins.
 """
 import math
@@ -144,6 +147,38 @@ def test_ex_accumulates(oracle_mod):
     np.testing.assert_allclose(acc["grad_bias"], db0 + base["grad_bias"], rtol=1e-14)
 
 
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_ex_nan_in_ignored_rows_changes_nothing(oracle_mod, reduction, with_bias):
+    """Poisoned ignored rows: every output bit-identical to the clean run, all finite."""
+    X, W, t, b = _case(BT=12, H=4, V=7, seed=17, frac=0.34)
+    tn = t.numpy()
+    ign = np.nonzero(tn == -100)[0]
+    assert ign.size >= 4
+    Xp = X.clone()
+    Xp[ign[0::2]] = float("nan")
+    Xp[ign[1::2]] = float("inf")
+    bias = b if with_bias else None
+    g = None
+    gp = None
+    if reduction == "none":
+        g = si.make_grad_output(t, "none", 17, scalar=1.0).numpy()
+        g = np.where(tn != -100, g, 0.5)
+        gp = np.where(tn != -100, g, np.nan)
+    kw = dict(bias=bias, z_loss_scale=0.05, reduction=reduction)
+    clean = oracle_mod.flce_ex(X, W, t, grad_output=g, **kw)
+    pois = oracle_mod.flce_ex(Xp, W, t, grad_output=gp, **kw)
+    for key in ("loss", "z_loss", "accuracy", "predicted", "dX", "dW", "grad_bias"):
+        a, c = clean[key], pois[key]
+        if a is None:
+            assert c is None and (key != "grad_bias" or not with_bias)
+            continue
+        a, c = np.asarray(a), np.asarray(c)
+        assert np.all(np.isfinite(c)), f"{key} not finite after poisoning ignored rows"
+        assert a.tobytes() == c.tobytes(), f"{key} changed by poisoned ignored rows"
+    assert np.all(pois["dX"][ign] == 0.0) and not np.any(np.signbit(pois["dX"][ign]))
+
+
 # ------------------------------------------------------------ planted mistakes
 MUTANTS_EX = [
     ("bias left out of the logits", "z[v] += bias[v];", "z[v] += 0.0 * bias[v];"),
@@ -151,8 +186,11 @@ MUTANTS_EX = [
     ("z-loss missing from the loss", "lrow[i] = l - z[t[i]] + lam * l * l;",
      "lrow[i] = l - z[t[i]];"),
     ("ties resolve to the last index", "if (z[v] > z[am]) am = v;", "if (z[v] >= z[am]) am = v;"),
-    ("grad_bias sums the wrong column", "for (int64_t i = 0; i < BT; ++i) a += G[i * V + v];",
-     "for (int64_t i = 0; i < BT; ++i) a += G[i * V + (v + 1) % V];"),
+    ("grad_bias sums the wrong column", "for (int64_t n = 0; n < N; ++n) a += G[idx[n] * V + v];",
+     "for (int64_t n = 0; n < N; ++n) a += G[idx[n] * V + (v + 1) % V];"),
+    ("grad_weight sums over every row, ignored ones included",
+     "for (int64_t n = 0; n < N; ++n) a += G[idx[n] * V + v] * X[idx[n] * H + k];",
+     "for (int64_t i = 0; i < BT; ++i) a += G[i * V + v] * X[i * H + k];"),
     ("accuracy reduced by the wrong count", "if (acc) acc[0] = d > 0.0 ? sa / d : 0.0;",
      "if (acc) acc[0] = d > 0.0 ? sa / (d + 1.0) : 0.0;"),
 ]
@@ -165,6 +203,8 @@ def _ex_pins_pass(oracle_mod) -> bool:
                 test_ex_against_torch(oracle_mod, red, lam)
             test_ex_per_token_outputs(oracle_mod, red)
         test_ex_ties_pick_lowest_index(oracle_mod)
+        for red in ("mean", "sum", "none"):
+            test_ex_nan_in_ignored_rows_changes_nothing(oracle_mod, red, True)
     except AssertionError:
         return False
     return True
