@@ -17,16 +17,23 @@ import torch
 from . import fused_linear_cross_entropy_fwd_bwd, scale_cast
 
 
-def _grads_to(dtype, g, tensors):
-    """Scale each fp32-or-native gradient by the device scalar g (None = 1) into dtype."""
+def _grads_to(dtype, g, tensors, owned: bool):
+    """Scale each fp32-or-native gradient by the device scalar g (None = 1) into dtype.
+
+    ``owned`` says the tensors are this backward's own (fresh from a library
+    call), so one already in ``dtype`` with no scale is returned as it is.
+    Tensors saved by the forward are never written: a second backward through
+    a retained graph must see them unchanged, and the returned gradient must
+    not share storage with them.
+    """
     out = []
     for t in tensors:
         if t is None:
             out.append(None)
-        elif g is None and t.dtype == dtype:
+        elif owned and g is None and t.dtype == dtype:
             out.append(t)
         else:
-            out.append(scale_cast(t, dtype, scale=g, out=t if t.dtype == dtype else None))
+            out.append(scale_cast(t, dtype, scale=g))
     return out
 
 
@@ -65,13 +72,13 @@ class FusedLinearCrossEntropy(torch.autograd.Function):
                 chunk_size=chunk_size, chunk_mem_const=chunk_mem_const, accum_dtype=accum_dtype,
                 frozen_weight=frozen, z_loss_scale=z_loss_scale, grad_output=go)
             dX, dW, db = r.dX, r.dW, r.grad_bias
-            dW, db = _grads_to(weight.dtype, None, [dW, db])
+            dW, db = _grads_to(weight.dtype, None, [dW, db], owned=True)
         else:
             dX, dW, db = ctx.saved_tensors
             g = grad_loss.reshape(1).float()
             dW = None if frozen else dW
             db = db if has_bias else None
-            dX, dW, db = _grads_to(dX.dtype, g, [dX, dW, db])
+            dX, dW, db = _grads_to(dX.dtype, g, [dX, dW, db], owned=False)
         return dX, dW, None, db, None, None, None, None, None, None, None
 
 

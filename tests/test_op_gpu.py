@@ -112,3 +112,46 @@ def test_opcheck(pkg):
              32, 1, True, False, 0.0)
     torch.library.opcheck(torch.ops.flce.fused_linear_cross_entropy_backward.default, gargs,
                           test_utils=("test_schema", "test_faketensor"))
+
+
+@pytest.mark.parametrize("entry", ["wrapper", "op"])
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_retained_graph_backward_twice(pkg, entry, reduction, dtype):
+    """Two backward passes through one retained graph, upstream gradient 2.0:
+    both give the oracle's gradients for that upstream gradient.  Backward must
+    not scale the tensors the forward saved (PR #1554, Tests: the none
+    reduction re-enters with reusable buffers; mean and sum keep the
+    forward's gradients), and the gradients it returns must not share
+    storage with them."""
+    X, W, t, b = _case(seed=23)
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    X, W, b = X.to(td), W.to(td), b.to(td)
+    dev = torch.device("cuda:0")
+    fn = (_wrapper if entry == "wrapper" else _op)(pkg, 0.0)
+    x = X.to(dev).requires_grad_(True)
+    w = W.to(dev).requires_grad_(True)
+    bb = b.to(dev).requires_grad_(True)
+    loss = fn(x, w, t.to(dev), bb, reduction)
+    if reduction == "none":
+        g = torch.where(t != -100, torch.full(t.shape, 2.0), torch.zeros(t.shape))
+    else:
+        g = torch.tensor([2.0])
+    gd = g.to(dev) if reduction == "none" else g.to(dev).reshape(())
+    ref = oracle.flce_ex(X, W, t, bias=b, reduction=reduction, grad_output=g.numpy())
+    tg = 1e-4 if dtype == "f32" else 2e-2
+    grads = []
+    for _ in range(2):
+        x.grad = w.grad = bb.grad = None
+        loss.backward(gd, retain_graph=True)
+        torch.cuda.synchronize()
+        grads.append((x.grad.clone(), w.grad.clone(), bb.grad.clone()))
+        assert _rel(x.grad.double().cpu(), ref["dX"]) <= tg
+        assert _rel(w.grad.double().cpu(), ref["dW"]) <= tg
+        assert _rel(bb.grad.double().cpu(), ref["grad_bias"]) <= tg
+        # writing into the returned gradients must not reach the saved state
+        x.grad.mul_(100.0)
+        w.grad.mul_(100.0)
+        bb.grad.mul_(100.0)
+    for a, c in zip(grads[0], grads[1]):
+        assert torch.equal(a, c)
