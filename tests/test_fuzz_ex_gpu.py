@@ -9,7 +9,10 @@ and bias gradients onto random buffers.  Checks as in the fixed cases: loss
 and z-loss to the loss tolerance, dX / dW / grad_bias to the gradient
 tolerance, exact zeros (and -1 predictions) at ignored rows, the predicted
 token equal to the oracle's wherever the top two logits are apart by more
-than fp32 accumulation can move, and the accuracy consistent with it.
+than fp32 accumulation can move, and the accuracy consistent with it.  In
+about half the cases the ignored rows of X hold NaN on the GPU (the oracle
+gets the clean rows): nothing of them may reach any output (PR #1554, Tests:
+ignored rows never enter the projection, with bias on and off).
 """
 import numpy as np
 import pytest
@@ -46,7 +49,8 @@ def draw(i):
                 want_z=bool(r.random() < 0.6), want_acc=bool(r.random() < 0.6),
                 want_pred=bool(r.random() < 0.6),
                 accumulate=bool(r.random() < 0.2),
-                seed=8000 + 13 * i)
+                seed=8000 + 13 * i,
+                poison=bool(r.random() < 0.5))
 
 
 @pytest.fixture(scope="module")
@@ -98,8 +102,11 @@ def test_random_options(pkg, i):
             db0 = torch.from_numpy(rng.standard_normal(V).astype(np.float32) * 0.01)
 
     dev = torch.device("cuda:0")
+    Xg = X.clone()
+    if c["poison"] and (~lab).any():
+        Xg[torch.from_numpy(~lab)] = float("nan")
     r = pkg.fused_linear_cross_entropy_fwd_bwd(
-        X.to(dev), W.to(dev), t.to(dev), bias=None if b is None else b.to(dev), ignore_index=ii,
+        Xg.to(dev), W.to(dev), t.to(dev), bias=None if b is None else b.to(dev), ignore_index=ii,
         reduction=red, chunk_size=c["chunk"], accum_dtype=acc_dt, grad_output=g.to(dev),
         forward_only=c["forward_only"], z_loss_scale=c["lam"], return_z_loss=c["want_z"],
         return_accuracy=c["want_acc"], return_predicted=c["want_pred"],

@@ -116,6 +116,54 @@ def test_bias_zloss_and_outputs(pkg, dtype, reduction, chunk):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_poisoned_ignored_rows_with_every_option(pkg, dtype, reduction):
+    """NaN and Inf in ignored X rows (and NaN in the upstream gradient there),
+    with the bias, a z-loss coefficient and every per-token output on: every
+    output bit-identical to the clean run, and within tolerance of the oracle
+    (PR #1554, Tests: ignored rows never enter the projection, with bias on
+    and off)."""
+    BT, H, V = 300, 96, 700
+    X, W, t, b = _case(BT, H, V, dtype, seed=29, frac=0.3)
+    lab = (t != -100).numpy()
+    ign = np.nonzero(~lab)[0]
+    Xp = X.clone()
+    Xp[torch.from_numpy(ign[0::2])] = float("nan")
+    Xp[torch.from_numpy(ign[1::2])] = float("inf")
+    lam = 1e-3
+    g = si.make_grad_output(t, "none", 29, scalar=1.0) if reduction == "none" else None
+    dev = torch.device("cuda:0")
+
+    def run(x):
+        r = pkg.fused_linear_cross_entropy_fwd_bwd(
+            x.to(dev), W.to(dev), t.to(dev), bias=b.to(dev), reduction=reduction,
+            chunk_size=64, accum_dtype=torch.float32, z_loss_scale=lam,
+            grad_output=None if g is None else g.to(dev), return_z_loss=True,
+            return_accuracy=True, return_predicted=True)
+        torch.cuda.synchronize()
+        return {k: getattr(r, k).cpu() for k in
+                ("loss", "z_loss", "accuracy", "predicted", "dX", "dW", "grad_bias")}
+
+    clean, pois = run(X), run(Xp)
+    for k in clean:
+        assert torch.isfinite(pois[k].double()).all(), k
+        assert clean[k].reshape(-1).view(torch.uint8).equal(pois[k].reshape(-1).view(torch.uint8)), k
+    gref = None if g is None else torch.nan_to_num(g).numpy()
+    ref = oracle.flce_ex(X, W, t, bias=b, z_loss_scale=lam, reduction=reduction,
+                         grad_output=gref)
+    tl, tg = TOL[dtype]
+    if reduction == "none":
+        assert _rel(pois["loss"].numpy()[lab], ref["loss"][lab]) <= tl
+    else:
+        assert abs(float(pois["loss"]) - ref["loss"]) <= tl * abs(ref["loss"])
+    assert np.all(pois["dX"].float().numpy()[~lab] == 0.0)
+    assert _rel(pois["dX"].double(), ref["dX"]) <= tg
+    assert _rel(pois["dW"].double(), ref["dW"]) <= tg
+    assert _rel(pois["grad_bias"].double(), ref["grad_bias"]) <= tg
+    assert np.all(pois["predicted"].numpy()[~lab] == -1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ties_resolve_to_lower_index(pkg, dtype):
     BT, H, V = 130, 64, 300
     X, W, t, b = _case(BT, H, V, dtype, seed=23, frac=0.0, ties=True)
