@@ -138,7 +138,14 @@ size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype
  *   W            [V, H]  dtype        lm_head weight
  *   targets      [BT]    int64        class ids; rows equal to ignore_index are
  *                                     ignored (any int64 value, default -100)
- *   BT, H, V                          BT >= 0, 8 <= H <= 2^20 and H % 8 == 0, V >= 1
+ *   BT, H, V                          BT >= 0, 8 <= H <= 2^20 and H % 8 == 0, V >= 1;
+ *                                     with gradients, 256 x round_up(V, 8) x itemsize
+ *                                     and (unless frozen) 256 x round_up(chunk, 8) x
+ *                                     itemsize must stay under 2 GiB (V <= 4194296 for
+ *                                     16-bit operands, 2097144 for fp32).  X may be of
+ *                                     any size; beyond 2 GiB - 64 KiB the workspace
+ *                                     also holds up to chunk x H x itemsize bytes of
+ *                                     gathered rows (at most 2 GiB)
  *   dtype                             FLCE_F32, FLCE_F16 or FLCE_BF16
  *   reduction                         FLCE_MEAN, FLCE_SUM or FLCE_NONE
  *   chunk_size, chunk_mem_const       see flce_chunk_size
@@ -203,8 +210,8 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
  *                 like the loss (the fraction or the count of correct rows).
  *   predicted     NULL, or [BT] int64: the lowest column holding the row's
  *                 largest logit (fp32), -1 at ignored rows (PR #1554, Details
- *                 item 1: ignored rows get 0 per-token loss, z-loss and
- *                 accuracy and -1 as predicted token).
+ *                 item 1: the per-token outputs of an ignored row are zero,
+ *                 and its predicted token is the sentinel -1).
  * Pointers are device pointers: bias and grad_bias 16-byte aligned,
  * predicted 8-byte, z_loss and accuracy 4-byte.
  */
@@ -225,6 +232,21 @@ typedef struct {
 size_t flce_workspace_bytes_ex(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,
                                int64_t chunk_size, int32_t chunk_mem_const,
                                const flce_options_t* opt);
+
+/*
+ * Where a call leaves its labelled-row index.  The row compaction of
+ * flce_fwd_bwd / flce_fwd_bwd_ex (PR #1554, Summary: nonzero() of the
+ * not-ignored mask supplies the rows the projections run on) writes the
+ * ascending list of labelled row ids as int32 into the workspace, and the
+ * chunk loop only reads it.  After a call with these arguments and options
+ * returns FLCE_OK, the workspace holds that list at this byte offset,
+ * stats.n_valid entries, valid in stream order until the workspace is
+ * reused.  The offset is a multiple of 256.  Returns (size_t)-1 for
+ * arguments flce_workspace_bytes_ex rejects.
+ */
+size_t flce_workspace_row_index_offset(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,
+                                       int64_t chunk_size, int32_t chunk_mem_const,
+                                       const flce_options_t* opt);
 
 /*
  * flce_fwd_bwd with the optional parts above; every other argument, the
@@ -255,10 +277,16 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
 int flce_scale_cast(const void* src, flce_dtype_t src_dtype, void* dst, flce_dtype_t dst_dtype,
                     int64_t n, const float* scale, void* stream);
 
-/* Human-readable name of a status code (static storage). */
+/* Error reporting.  The pages say nothing about how a native library reports
+ * failure; these two serve the status codes above, which every entry point
+ * returns instead of throwing.
+ * flce_status_string: human-readable name of a status code (static storage;
+ * "unknown status" for other values). */
 const char* flce_status_string(int status);
 
-/* Detail of the last FLCE_E_HIP error raised on the calling thread. */
+/* Detail of the last FLCE_E_HIP error raised on the calling thread: the
+ * failing HIP call and its error string (thread-local storage, overwritten
+ * by the thread's next FLCE_E_HIP; empty before the first). */
 const char* flce_last_error(void);
 
 /* ------------------------------------------------------------------------

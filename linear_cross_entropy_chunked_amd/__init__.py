@@ -26,8 +26,9 @@ KERNEL_KINDS = ["mask_scan", "zero_ignored_rows", "logits_gemm", "softmax_grad",
                 "bias_grad"]
 
 # Every symbol include/flce.h declares.
-EXPORTS = ["flce_chunk_size", "flce_chunk_size_mi355x", "flce_workspace_bytes", "flce_fwd_bwd", "flce_workspace_bytes_ex",
-           "flce_fwd_bwd_ex", "flce_scale_cast", "flce_status_string", "flce_last_error",
+EXPORTS = ["flce_chunk_size", "flce_chunk_size_mi355x", "flce_workspace_bytes", "flce_fwd_bwd",
+           "flce_workspace_bytes_ex", "flce_workspace_row_index_offset", "flce_fwd_bwd_ex",
+           "flce_scale_cast", "flce_status_string", "flce_last_error",
            "flce_profile_begin", "flce_profile_begin_kinds", "flce_profile_end",
            "flce_kernel_name"]
 
@@ -87,6 +88,9 @@ def load():
     lib.flce_workspace_bytes_ex.argtypes = [I64, I64, I64, I, I64, I32,
                                             ctypes.POINTER(FlceOptions)]
     lib.flce_workspace_bytes_ex.restype = SZ
+    lib.flce_workspace_row_index_offset.argtypes = [I64, I64, I64, I, I64, I32,
+                                                    ctypes.POINTER(FlceOptions)]
+    lib.flce_workspace_row_index_offset.restype = SZ
     lib.flce_fwd_bwd_ex.argtypes = [P, P, P, I64, I64, I64, I, I64, I, I64, I32, I, I32, I32, P,
                                     P, P, P, P, SZ, P, ctypes.POINTER(FlceStats),
                                     ctypes.POINTER(FlceOptions)]
@@ -141,6 +145,14 @@ def flce_workspace_bytes_ex(BT: int, H: int, V: int, dtype: int, chunk_size: int
                             chunk_mem_const: int = 1, opt: FlceOptions | None = None) -> int:
     return load().flce_workspace_bytes_ex(BT, H, V, dtype, chunk_size, chunk_mem_const,
                                           ctypes.byref(opt) if opt is not None else None)
+
+
+def flce_workspace_row_index_offset(BT: int, H: int, V: int, dtype: int, chunk_size: int = 0,
+                                    chunk_mem_const: int = 1,
+                                    opt: FlceOptions | None = None) -> int:
+    return load().flce_workspace_row_index_offset(
+        BT, H, V, dtype, chunk_size, chunk_mem_const,
+        ctypes.byref(opt) if opt is not None else None)
 
 
 def flce_fwd_bwd_ex(X: int, W: int, targets: int, BT: int, H: int, V: int, dtype: int,
@@ -218,6 +230,7 @@ class FlceResult:
     z_loss: "object" = None
     accuracy: "object" = None
     predicted: "object" = None
+    row_index: "object" = None
 
 
 def fused_linear_cross_entropy_fwd_bwd(x, weight, target, *, bias=None, ignore_index: int = -100,
@@ -229,7 +242,8 @@ def fused_linear_cross_entropy_fwd_bwd(x, weight, target, *, bias=None, ignore_i
                                        return_z_loss: bool = False,
                                        return_accuracy: bool = False,
                                        return_predicted: bool = False, grad_bias=None,
-                                       workspace=None, stream=None) -> FlceResult:
+                                       workspace=None, stream=None,
+                                       return_row_index: bool = False) -> FlceResult:
     """Loss, dX and dW (and optionally grad_bias and per-token outputs) in one call.
 
     x [BT, H], weight [V, H] (float32, float16 or bfloat16, on the GPU),
@@ -242,6 +256,8 @@ def fused_linear_cross_entropy_fwd_bwd(x, weight, target, *, bias=None, ignore_i
     BT), or "mi355x" (or -1) for the MI355X policy.  ``forward_only``
     computes the loss (and the requested per-token outputs) only.
     ``z_loss_scale`` adds lam * lse^2 to every labelled row's loss.
+    ``return_row_index`` returns the call's ascending labelled-row index
+    (int32 [n_valid]) as a view of the workspace.
     """
     import torch
     if not (x.is_cuda and weight.is_cuda and target.is_cuda):
@@ -309,9 +325,13 @@ def fused_linear_cross_entropy_fwd_bwd(x, weight, target, *, bias=None, ignore_i
     if rc != 0:
         raise FlceError(rc, "flce_fwd_bwd_ex")
     one = (lambda a: a) if red == NONE else (lambda a: None if a is None else a[0])
+    row_index = None
+    if return_row_index:
+        off = flce_workspace_row_index_offset(BT, H, V, dt, cs, chunk_mem_const, opt)
+        row_index = workspace[off:off + 4 * st.n_valid].view(torch.int32)
     return FlceResult(loss=one(loss), dX=dX, dW=None if frozen_weight else dW,
                       stats=st.as_dict(), grad_bias=grad_bias, z_loss=one(zl),
-                      accuracy=one(acc), predicted=pred)
+                      accuracy=one(acc), predicted=pred, row_index=row_index)
 
 
 def scale_cast(src, dtype, scale=None, out=None):

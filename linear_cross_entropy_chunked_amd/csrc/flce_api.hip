@@ -50,6 +50,7 @@ int64_t chunk_rows(int64_t BT, int64_t H, int64_t V, int64_t chunk_size, int32_t
 // ---------------------------------------------------------- workspace layout
 constexpr int64_t kAlign = 256;
 constexpr uint64_t kMaxOperandBytes = 0x7fff0000ull;  // 2 GiB - 64 KiB
+constexpr uint64_t kMaxRangeBytes = 0x7ffffff0ull;    // largest range of one buffer descriptor
 constexpr int kDxCUs = 256;  // split k until every resident workgroup slot of 256 CUs is busy
 constexpr int64_t kDxMinKPerSplit = 1024;
 constexpr int kDxMaxSplits = 32;
@@ -65,11 +66,13 @@ constexpr size_t kDefaultSlabBudget = 2ull << 30;  // 2 GiB logits slab
 
 struct Layout {
   int64_t c = 0, ldz = 0, ldx = 0, stats_ld = 0;
+  bool x_gather = false;  // X exceeds one 32-bit range: logits read rows gathered into Xc
+  int64_t xc_rows = 0;    // rows gathered (and multiplied) at a time in that case
   int splits = 1;
   int64_t k_per_split = 0;
   size_t off_slab = 0, off_xct = 0, off_stats = 0, off_ztgt = 0, off_partial = 0, off_idx = 0,
          off_lossrow = 0, off_flags = 0, off_amax = 0, off_bias = 0, off_zrow = 0,
-         off_accrow = 0, total = 0;
+         off_accrow = 0, off_xc = 0, total = 0;
 };
 
 // What the options add to a call.
@@ -124,6 +127,13 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t c, const
   L.off_bias = take(x.bias_grad ? (size_t)ceil_div(c, kBiasRows) * L.ldz * 4 : 0);
   L.off_zrow = take(x.zrow ? nrow * 4 : 0);
   L.off_accrow = take(x.accrow ? nrow * 4 : 0);
+  L.x_gather = (uint64_t)BT * (uint64_t)H * itemsize(dtype) > kMaxOperandBytes;
+  if (L.x_gather) {
+    // whole 256-row tiles whose gathered rows fit one range (H <= 2^20: >= 256 rows)
+    const int64_t fit = (int64_t)(kMaxOperandBytes / ((uint64_t)H * itemsize(dtype))) / 256 * 256;
+    L.xc_rows = c < fit ? c : fit;
+  }
+  L.off_xc = take(L.x_gather ? (size_t)L.xc_rows * H * itemsize(dtype) : 0);
   L.total = off;
   return L;
 }
@@ -256,6 +266,15 @@ size_t flce_workspace_bytes_ex(int64_t BT, int64_t H, int64_t V, flce_dtype_t dt
   return make_layout(BT, H, V, dtype, c, extras_of(opt)).total;
 }
 
+size_t flce_workspace_row_index_offset(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,
+                                       int64_t chunk_size, int32_t chunk_mem_const,
+                                       const flce_options_t* opt) {
+  if (dtype < FLCE_F32 || dtype > FLCE_BF16) return (size_t)-1;
+  const int64_t c = chunk_rows(BT, H, V, chunk_size, chunk_mem_const);
+  if (c < 1) return (size_t)-1;
+  return make_layout(BT, H, V, dtype, c, extras_of(opt)).off_idx;
+}
+
 size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, flce_dtype_t dtype,
                             int64_t chunk_size, int32_t chunk_mem_const) {
   return flce_workspace_bytes_ex(BT, H, V, dtype, chunk_size, chunk_mem_const, nullptr);
@@ -333,13 +352,17 @@ int flce_scale_cast(const void* src, flce_dtype_t src_dtype, void* dst, flce_dty
   return FLCE_OK;
 }
 
-int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
-                    int64_t V, flce_dtype_t dtype, int64_t ignore_index,
-                    flce_reduction_t reduction, int64_t chunk_size, int32_t chunk_mem_const,
-                    flce_dtype_t accum_dtype, int32_t frozen_weight, int32_t accumulate_dw,
-                    const float* grad_output, float* loss, void* dX, void* dW, void* workspace,
-                    size_t workspace_bytes, void* stream, flce_stats_t* stats,
-                    const flce_options_t* opt) {
+}  // extern "C"
+
+namespace {
+
+// The whole call.
+int fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
+            int64_t V, flce_dtype_t dtype, int64_t ignore_index, flce_reduction_t reduction,
+            int64_t chunk_size, int32_t chunk_mem_const, flce_dtype_t accum_dtype,
+            int32_t frozen_weight, int32_t accumulate_dw, const float* grad_output, float* loss,
+            void* dX, void* dW, void* workspace, size_t workspace_bytes, void* stream,
+            flce_stats_t* stats, const flce_options_t* opt) {
   // ---- host-side checks: nothing is launched or written on failure
   if (dtype < FLCE_F32 || dtype > FLCE_BF16) return FLCE_E_DTYPE;
   if (accum_dtype != dtype && accum_dtype != FLCE_F32) return FLCE_E_DTYPE;
@@ -367,10 +390,18 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
   if (BT > 0 && (!X || !W || !targets || (grads && !dX))) return FLCE_E_ARG;
   if (BT > 0 && (!aligned(X, 16) || !aligned(W, 16) || (grads && !aligned(dX, 16))))
     return FLCE_E_ARG;
-  // The kernels address X and the logits slab with 32-bit byte offsets.
-  if ((uint64_t)BT * (uint64_t)H * itemsize(dtype) > kMaxOperandBytes) return FLCE_E_ARG;
   const int64_t c = chunk_rows(BT, H, V, chunk_size, chunk_mem_const);
   if (c < 1) return FLCE_E_ARG;
+  // The GEMMs address their operands through 32-bit buffer ranges of one
+  // tile: 256 rows of the logits slab (grad_input) and 256 hidden units of
+  // the transposed chunk rows (grad_weight).  X of any size: when it exceeds
+  // one range, the logits GEMM reads the chunk's rows gathered into the
+  // workspace, a range-sized block of rows at a time.
+  {
+    const uint64_t s = itemsize(dtype);
+    if (grads && 256ull * (uint64_t)round_up(V, 8) * s > kMaxRangeBytes) return FLCE_E_ARG;
+    if (want_dw && 256ull * (uint64_t)round_up(c, 8) * s > kMaxRangeBytes) return FLCE_E_ARG;
+  }
   const Extras ext = extras_of(&o);
   const Layout L = make_layout(BT, H, V, dtype, c, ext);
   if (!workspace || !aligned(workspace, kAlign)) return FLCE_E_ARG;
@@ -421,6 +452,7 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
   float* bias_partial = reinterpret_cast<float*>(ws + L.off_bias);
   float* zrow = ext.zrow ? reinterpret_cast<float*>(ws + L.off_zrow) : nullptr;
   float* accrow = ext.accrow ? reinterpret_cast<float*>(ws + L.off_accrow) : nullptr;
+  void* xc = ws + L.off_xc;
   const bool none = reduction == FLCE_NONE;
 
   if (stats) {
@@ -451,13 +483,13 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
         return fail_hip(e, "hipHostMalloc");
       }
     }
-    hipError_t e = hipMemcpyAsync(g_host_flags, dflags, sizeof(ScanFlags), hipMemcpyDeviceToHost,
-                                  st);
+    ScanFlags* hf = g_host_flags;
+    hipError_t e = hipMemcpyAsync(hf, dflags, sizeof(ScanFlags), hipMemcpyDeviceToHost, st);
     if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(flags)");
     e = hipStreamSynchronize(st);
     if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
-    if (g_host_flags->bad_target) return FLCE_E_TARGET;
-    N = g_host_flags->n_valid;
+    if (hf->bad_target) return FLCE_E_TARGET;
+    N = hf->n_valid;
   }
   const int64_t chunks = ceil_div(N, c);
   if (stats) {
@@ -488,6 +520,7 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
 
     LogitsArgs la;
     la.X = X;
+    la.x_gathered = 0;
     la.W = W;
     la.idx = cidx;
     la.targets = targets;
@@ -503,7 +536,26 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
     la.bias = o.bias;
     la.amax = amax;
     la.store_slab = grads ? 1 : 0;
-    FLCE_LAUNCH(FLCE_K_LOGITS, launch_logits(dt, la, st));
+    if (!L.x_gather) {
+      FLCE_LAUNCH(FLCE_K_LOGITS, launch_logits(dt, la, st));
+    } else {
+      // X beyond one 32-bit range: gather a block of the chunk's rows, then
+      // multiply that block into its rows of the slab and statistics.
+      for (int64_t r0 = 0; r0 < rows; r0 += L.xc_rows) {
+        const int nr = (int)((rows - r0) < L.xc_rows ? (rows - r0) : L.xc_rows);
+        FLCE_LAUNCH(FLCE_K_GATHER, launch_gather_rows(dt, X, cidx + r0, nr, H, xc, st));
+        LogitsArgs lb = la;
+        lb.X = xc;
+        lb.x_gathered = 1;
+        lb.idx = cidx + r0;
+        lb.rows = nr;
+        lb.slab = static_cast<unsigned char*>(slab) + (size_t)r0 * L.ldz * itemsize(dt);
+        lb.stats = stats_buf + (size_t)r0 * L.stats_ld * 2;
+        lb.ztgt = ztgt + r0;
+        lb.amax = amax ? amax + (size_t)r0 * L.stats_ld : nullptr;
+        FLCE_LAUNCH(FLCE_K_LOGITS, launch_logits(dt, lb, st));
+      }
+    }
 
     SoftmaxArgs sa;
     sa.slab = slab;
@@ -611,15 +663,31 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
   return FLCE_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
+                    int64_t V, flce_dtype_t dtype, int64_t ignore_index,
+                    flce_reduction_t reduction, int64_t chunk_size, int32_t chunk_mem_const,
+                    flce_dtype_t accum_dtype, int32_t frozen_weight, int32_t accumulate_dw,
+                    const float* grad_output, float* loss, void* dX, void* dW, void* workspace,
+                    size_t workspace_bytes, void* stream, flce_stats_t* stats,
+                    const flce_options_t* opt) {
+  return fwd_bwd(X, W, targets, BT, H, V, dtype, ignore_index, reduction, chunk_size,
+                 chunk_mem_const, accum_dtype, frozen_weight, accumulate_dw, grad_output, loss, dX,
+                 dW, workspace, workspace_bytes, stream, stats, opt);
+}
+
 int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
                  int64_t V, flce_dtype_t dtype, int64_t ignore_index, flce_reduction_t reduction,
                  int64_t chunk_size, int32_t chunk_mem_const, flce_dtype_t accum_dtype,
                  int32_t frozen_weight, int32_t accumulate_dw, const float* grad_output,
                  float* loss, void* dX, void* dW, void* workspace, size_t workspace_bytes,
                  void* stream, flce_stats_t* stats) {
-  return flce_fwd_bwd_ex(X, W, targets, BT, H, V, dtype, ignore_index, reduction, chunk_size,
-                         chunk_mem_const, accum_dtype, frozen_weight, accumulate_dw, grad_output,
-                         loss, dX, dW, workspace, workspace_bytes, stream, stats, nullptr);
+  return fwd_bwd(X, W, targets, BT, H, V, dtype, ignore_index, reduction, chunk_size,
+                 chunk_mem_const, accum_dtype, frozen_weight, accumulate_dw, grad_output, loss, dX,
+                 dW, workspace, workspace_bytes, stream, stats, nullptr);
 }
 
 }  // extern "C"

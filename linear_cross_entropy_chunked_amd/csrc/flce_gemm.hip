@@ -673,9 +673,12 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
   const S* X = static_cast<const S*>(a.X);
   const S* W = static_cast<const S*>(a.W);
 
-  // X: gathered rows anywhere in [BT, H]; W: this tile's rows [n0, n0 + BN).
+  // X: gathered rows anywhere in [BT, H] (one 32-bit range over all of X),
+  // or, when X is larger than that, the chunk's rows gathered beforehand
+  // into [rows, H]; W: this tile's rows [n0, n0 + BN).
   const uint32_t row_bytes = (uint32_t)a.H * (uint32_t)sizeof(S);
-  const desc_t xr = make_rsrc(X, (uint64_t)a.BT * a.H * sizeof(S));
+  const desc_t xr =
+      make_rsrc(X, (uint64_t)(a.x_gathered ? (int64_t)a.rows : a.BT) * a.H * sizeof(S));
   const int64_t nrows_w = a.V - n0 < C::BN ? a.V - n0 : C::BN;
   const desc_t wr = make_rsrc(W + n0 * a.H, (uint64_t)nrows_w * a.H * sizeof(S));
   OA la;
@@ -692,9 +695,14 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
     const int m = tid + i * C::NT, gm = m0 + m;
     tix[i] = a.idx[m < C::BM && gm < a.rows ? gm : 0];
   }
-  la.init_indexed(
-      tid, [&](int r) -> uint32_t { return (uint32_t)a.idx[m0 + r < a.rows ? m0 + r : 0]; },
-      [&](int r, uint32_t e) -> uint32_t { return m0 + r < a.rows ? e * row_bytes : kOOB; });
+  if (a.x_gathered)
+    la.init(tid, [&](int r) -> uint32_t {
+      return m0 + r < a.rows ? (uint32_t)(m0 + r) * row_bytes : kOOB;
+    });
+  else
+    la.init_indexed(
+        tid, [&](int r) -> uint32_t { return (uint32_t)a.idx[m0 + r < a.rows ? m0 + r : 0]; },
+        [&](int r, uint32_t e) -> uint32_t { return m0 + r < a.rows ? e * row_bytes : kOOB; });
   lb.init(tid, [&](int r) -> uint32_t { return r < nrows_w ? (uint32_t)r * row_bytes : kOOB; });
   int64_t tgt[TPT];
 #pragma unroll

@@ -7,9 +7,10 @@ namespace flce {
 
 // Logits GEMM of one chunk (rows = labelled rows in this chunk).
 struct LogitsArgs {
-  const void* X;           // [BT, H] operand dtype
+  const void* X;           // [BT, H] operand dtype, or with x_gathered the chunk's rows [rows, H]
   const void* W;           // [V, H]
   const int32_t* idx;      // [rows] labelled row ids of this chunk
+  int x_gathered;          // 1: row r of the chunk is row r of X (already gathered)
   const int64_t* targets;  // [BT]
   int rows;
   int64_t BT, H, V;
@@ -120,6 +121,9 @@ hipError_t launch_mask_scan(const int64_t* targets, int64_t BT, int64_t V, int64
                             int32_t* idx, ScanFlags* flags, hipStream_t st);
 hipError_t launch_gather_t(int dtype, const void* X, const int32_t* idx, int rows, int64_t H,
                            void* XcT, int64_t ldx, hipStream_t st);
+// Xc[r, :] = X[idx[r], :] for r < rows (row-major, H elements per row).
+hipError_t launch_gather_rows(int dtype, const void* X, const int32_t* idx, int rows, int64_t H,
+                              void* Xc, hipStream_t st);
 // Outputs of an ignored row: zero dX row (dX may be NULL), and, where given,
 // zero per-token loss / z-loss / accuracy and -1 as predicted token.
 struct IgnoredOut {

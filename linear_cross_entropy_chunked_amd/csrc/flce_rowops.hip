@@ -130,6 +130,31 @@ hipError_t launch_gather_t(int dtype, const void* X, const int32_t* idx, int row
 }
 
 // ---------------------------------------------------------------------------
+// Row gather, row-major: Xc[r, :] = X[idx[r], :] for r < rows.  Used when X
+// is larger than one 32-bit buffer range, so that the logits GEMM can read
+// the chunk's rows with small offsets.  One 16-byte vector per thread and
+// step; a workgroup walks a row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4_t* __restrict__ X,
+                                                          const int32_t* __restrict__ idx,
+                                                          int64_t row_vecs,
+                                                          u32x4_t* __restrict__ Xc) {
+  const int r = blockIdx.x;
+  const u32x4_t* src = X + (int64_t)idx[r] * row_vecs;
+  u32x4_t* dst = Xc + (int64_t)r * row_vecs;
+  for (int64_t v = threadIdx.x; v < row_vecs; v += blockDim.x) dst[v] = src[v];
+}
+
+hipError_t launch_gather_rows(int dtype, const void* X, const int32_t* idx, int rows, int64_t H,
+                              void* Xc, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t row_vecs = H * (dtype == 0 ? 4 : 2) / 16;  // H % 8 == 0
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)rows), dim3(256), 0, st,
+                     static_cast<const u32x4_t*>(X), idx, row_vecs, static_cast<u32x4_t*>(Xc));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Ignored rows get a +0.0 grad_input row and +0.0 per-token loss (PR #1554,
 // Details item 1).  Labelled rows are left alone: the projections write them.
 // ---------------------------------------------------------------------------

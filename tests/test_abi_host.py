@@ -164,6 +164,43 @@ def test_overlapping_buffers_rejected_on_host(flce_lib, kw):
     assert _call(flce_lib, workspace_bytes=1, frozen_weight=1, dW=FAKE["W"]) == -4
 
 
+# Disjoint fake addresses 1 TiB apart, for the large shapes below (never
+# dereferenced: the workspace is always declared too small).
+FAR = {k: (i + 1) << 40 for i, k in enumerate(FAKE)}
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(V=4194296), -4),                        # 256 slab rows of bf16 fit one 32-bit range
+    (dict(V=4194304), -1),                        # ... and no longer
+    (dict(V=2097144, dtype=0, accum_dtype=0), -4),
+    (dict(V=2097152, dtype=0, accum_dtype=0), -1),
+    (dict(V=4194304, frozen_weight=1, dW=None), -1),  # grad_input still reads the slab
+    (dict(BT=1 << 20, H=2048, chunk_size=1024), -4),  # X of 4 GiB: rows gathered per chunk
+    (dict(BT=1 << 20, H=2048, chunk_size=1 << 20, frozen_weight=1, dW=None), -4),  # 4 GiB chunk
+])
+def test_size_limits_on_host(flce_lib, kw, status):
+    """The 32-bit buffer ranges of one GEMM tile bound V and the chunk, not X."""
+    a = dict(FAR, BT=4, H=64, V=10, dtype=flce_lib.BF16, ignore_index=-100, reduction=0,
+             chunk_size=0, chunk_mem_const=1, accum_dtype=flce_lib.BF16, frozen_weight=0,
+             accumulate_dw=0, grad_output=None, workspace_bytes=1, stream=None)
+    a.update(kw)
+    assert flce_lib.flce_fwd_bwd(**a) == status
+
+
+def test_row_index_offset(flce_lib):
+    """The labelled-row index sits 256-byte aligned inside the workspace, with
+    room for BT int32 entries, for every option set."""
+    O = flce_lib.FlceOptions
+    for args in [(8192, 4096, 128256, flce_lib.BF16, 2048, 1), (300, 96, 700, flce_lib.F32, 64, 1),
+                 (1, 8, 1, flce_lib.F16, 0, 1), (1 << 20, 2048, 1000, flce_lib.BF16, 1024, 1)]:
+        for opt in (None, O(1), O(0, None, 16, 0.0, 16, 16, 16)):
+            off = flce_lib.flce_workspace_row_index_offset(*args, opt)
+            ws = flce_lib.flce_workspace_bytes_ex(*args, opt)
+            assert off % 256 == 0 and off + 4 * args[0] <= ws, (args, off, ws)
+    assert flce_lib.flce_workspace_row_index_offset(128, 64, 100, 7, 64, 1, None) == 2 ** 64 - 1
+    assert flce_lib.flce_workspace_row_index_offset(128, 0, 100, 0, 64, 1, None) == 2 ** 64 - 1
+
+
 # ----------------------------------------------------------------- options
 def test_workspace_ex_follows_options(flce_lib):
     """No options: the plain size.  Loss only: no slab.  Extras: small additions."""
