@@ -299,6 +299,73 @@ def flce_matmul(X, W, targets, *, ignore_index: int = -100, reduction: str = "me
     return dict(loss=loss, dX=dX, dW=dW, lse=lse_full, n_valid=N)
 
 
+def _row_scales(t, rows, n_valid: int, reduction: str, g):
+    """s_i for the given labelled rows: g/N (mean), g (sum), g_i (none)."""
+    if reduction == "none":
+        return np.ones(rows.size) if g is None else g[rows]
+    gs = 1.0 if g is None else float(g[0])
+    return np.full(rows.size, gs / n_valid if reduction == "mean" else gs)
+
+
+def dx_rows_matmul(Xd: np.ndarray, Wd: np.ndarray, targets, rows, *, n_valid: int,
+                   ignore_index: int = -100, reduction: str = "mean", grad_output=None,
+                   rows_per_block: int = 64):
+    """``dx_rows`` with numpy fp64 matrix products: (dX rows [R,H], loss [R], lse [R]).
+
+    Per selected labelled row i: z = X_i W^T, lse, loss = lse - z_t, and
+    dX_i = s_i (softmax(z) - onehot(t_i)) W.  Ignored rows give +0.0, loss 0
+    and NaN lse.  Blocks of rows only bound memory.
+    """
+    t = _i64(targets)
+    r = _i64(rows)
+    g = _grad(grad_output, reduction, Xd.shape[0])
+    H = Xd.shape[1]
+    dx = np.zeros((r.size, H))
+    lr = np.zeros(r.size)
+    ls = np.full(r.size, np.nan)
+    lab = np.nonzero(t[r] != ignore_index)[0]
+    for s0 in range(0, lab.size, rows_per_block):
+        sel = lab[s0:s0 + rows_per_block]
+        ri = r[sel]
+        Z = Xd[ri] @ Wd.T
+        l = _logsumexp_rows(Z)
+        k = np.arange(sel.size)
+        lr[sel] = l - Z[k, t[ri]]
+        ls[sel] = l
+        G = np.exp(Z - l[:, None])
+        G[k, t[ri]] -= 1.0
+        G *= _row_scales(t, ri, n_valid, reduction, g)[:, None]
+        dx[sel] = G @ Wd
+    return dx, lr, ls
+
+
+def dw_rows_matmul(Xd: np.ndarray, Wd: np.ndarray, targets, vrows, lse_all, *, n_valid: int,
+                   ignore_index: int = -100, reduction: str = "mean", grad_output=None,
+                   rows_per_block: int = 2048):
+    """``dw_rows`` with numpy fp64 matrix products: dW rows [R,H] for vocabulary rows vrows.
+
+    dW_v = sum over labelled i of s_i (exp(z_iv - lse_i) - [t_i == v]) X_i,
+    with z_iv = X_i . W_v and lse the given per-row log-sum-exp.  Only labelled
+    rows enter (an ignored row is never read).  Row blocks only bound memory;
+    each block's product is added in ascending row order.
+    """
+    t = _i64(targets)
+    v = _i64(vrows)
+    g = _grad(grad_output, reduction, Xd.shape[0])
+    lse_all = np.asarray(lse_all, dtype=np.float64)
+    lab = np.nonzero(t != ignore_index)[0]
+    out = np.zeros((v.size, Xd.shape[1]))
+    Wv = Wd[v]
+    for s0 in range(0, lab.size, rows_per_block):
+        ri = lab[s0:s0 + rows_per_block]
+        Xi = Xd[ri]
+        G = np.exp(Xi @ Wv.T - lse_all[ri][:, None])
+        G -= (t[ri][:, None] == v[None, :])
+        G *= _row_scales(t, ri, n_valid, reduction, g)[:, None]
+        out += G.T @ Xi
+    return out
+
+
 def target_logits(Xd: np.ndarray, Wd: np.ndarray, targets, *, ignore_index: int = -100):
     """z[i, t_i] = X_i . W_{t_i} for labelled rows (fp64; 0 for ignored rows)."""
     t = _i64(targets)

@@ -321,6 +321,39 @@ def test_matmul_variant_matches_loops(oracle_mod, reduction):
     assert np.all(np.isnan(lse_m[~lab])) and np.all(np.isnan(lse_l[~lab]))
 
 
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_matmul_row_subsets_match_loops(oracle_mod, reduction):
+    """The matmul forms of the per-row oracle functions (used at full size)
+    equal the loop forms on selected rows, ignored ones included."""
+    X, W, t = _case(BT=41, H=10, V=19, seed=27, frac=0.3)
+    g = si.make_grad_output(t, reduction, seed=27, scalar=1.1)
+    Xd, Wd = oracle_mod.widen(X), oracle_mod.widen(W)
+    full = oracle_mod.flce(X, W, t, reduction=reduction, grad_output=g)
+    N = full["n_valid"]
+    rows = np.array([0, 3, 4, 11, 12, 25, 40])
+    a = oracle_mod.dx_rows(X, W, t, rows, n_valid=N, reduction=reduction, grad_output=g)
+    b = oracle_mod.dx_rows_matmul(Xd, Wd, t, rows, n_valid=N, reduction=reduction,
+                                  grad_output=g, rows_per_block=3)
+    np.testing.assert_allclose(b[0], a[0], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(b[1], a[1], rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(np.isnan(b[2]), np.isnan(a[2]))
+    np.testing.assert_allclose(b[2][~np.isnan(a[2])], a[2][~np.isnan(a[2])], rtol=1e-14)
+    np.testing.assert_allclose(b[0], full["dX"][rows], rtol=1e-12, atol=1e-15)
+    vrows = np.array([0, 1, 7, 18, int(t[2]) if int(t[2]) >= 0 else 5])
+    lse = full["lse"]
+    c = oracle_mod.dw_rows(X, W, t, vrows, lse, n_valid=N, reduction=reduction, grad_output=g)
+    d = oracle_mod.dw_rows_matmul(Xd, Wd, t, vrows, lse, n_valid=N, reduction=reduction,
+                                  grad_output=g, rows_per_block=5)
+    np.testing.assert_allclose(d, c, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(d, full["dW"][vrows], rtol=1e-12, atol=1e-15)
+    # an ignored X row full of NaN is never read
+    Xp = Xd.copy()
+    Xp[np.nonzero(t.numpy() == -100)[0]] = np.nan
+    e = oracle_mod.dw_rows_matmul(Xp, Wd, t, vrows, lse, n_valid=N, reduction=reduction,
+                                  grad_output=g, rows_per_block=5)
+    assert e.tobytes() == d.tobytes()
+
+
 @pytest.mark.parametrize("reduction", ["mean", "none"])
 def test_row_subsets_match_full(oracle_mod, reduction):
     X, W, t = _case(BT=33, H=8, V=15, seed=26, frac=0.25)
