@@ -264,6 +264,39 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
                     const flce_options_t* opt);
 
 /*
+ * flce_fwd_bwd_ex without a workspace argument, for callers that cannot
+ * allocate device memory (tight serving loops, harnesses that forbid
+ * allocation).  The workspace is a static device array of
+ * FLCE_SCRATCH_BYTES inside the library: one per GPU, at its own address,
+ * taken when the library's code is loaded on that GPU and held until the
+ * process ends.  The call allocates nothing, device or host (the one host
+ * sync reads into plain host memory).  It still blocks once at that sync,
+ * so it cannot be captured into a HIP graph.
+ *
+ * Arguments, results, the sync, the errors and the stream semantics are
+ * flce_fwd_bwd_ex's.  In addition:
+ *   - a call whose flce_workspace_bytes_ex exceeds FLCE_SCRATCH_BYTES
+ *     returns FLCE_E_WORKSPACE before any launch (flce_last_error says how
+ *     much it needs; a smaller chunk_size needs less);
+ *   - the stream must run on the current device (else FLCE_E_ARG): the
+ *     current device's array is used;
+ *   - every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero: each call
+ *     writes every part before reading it).  Calls that overlap on one GPU,
+ *     from several host threads or on several streams without ordering
+ *     between them, race on it and must be serialised by the caller.
+ */
+#define FLCE_SCRATCH_BYTES (256ull << 20)
+
+int flce_fwd_bwd_ex_noalloc(const void* X, const void* W, const int64_t* targets, int64_t BT,
+                            int64_t H, int64_t V, flce_dtype_t dtype, int64_t ignore_index,
+                            flce_reduction_t reduction, int64_t chunk_size,
+                            int32_t chunk_mem_const, flce_dtype_t accum_dtype,
+                            int32_t frozen_weight, int32_t accumulate_dw,
+                            const float* grad_output, float* loss, void* dX, void* dW,
+                            void* stream, flce_stats_t* stats, const flce_options_t* opt);
+
+/*
  * dst[i] = scale * src[i], converted to dst_dtype: the product is rounded to
  * fp32, then to dst_dtype (round to nearest even).  Serves the wrapper's two
  * elementwise steps: the final cast of an fp32 grad_weight to the weight
@@ -284,9 +317,10 @@ int flce_scale_cast(const void* src, flce_dtype_t src_dtype, void* dst, flce_dty
  * "unknown status" for other values). */
 const char* flce_status_string(int status);
 
-/* Detail of the last FLCE_E_HIP error raised on the calling thread: the
- * failing HIP call and its error string (thread-local storage, overwritten
- * by the thread's next FLCE_E_HIP; empty before the first). */
+/* Detail of the last error raised on the calling thread with a message:
+ * every FLCE_E_HIP (the failing HIP call and its error string) and the
+ * refusals of flce_fwd_bwd_ex_noalloc (thread-local storage, overwritten by
+ * the next such error; empty before the first). */
 const char* flce_last_error(void);
 
 /* ------------------------------------------------------------------------

@@ -17,6 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libflce.so")
 
 F32, F16, BF16 = 0, 1, 2
+SCRATCH_BYTES = 256 << 20  # FLCE_SCRATCH_BYTES: the static workspace of flce_fwd_bwd_ex_noalloc
 MEAN, SUM, NONE = 0, 1, 2
 REDUCTIONS = {"mean": MEAN, "sum": SUM, "none": NONE}
 STATUS = {0: "FLCE_OK", -1: "FLCE_E_ARG", -2: "FLCE_E_DTYPE", -3: "FLCE_E_TARGET",
@@ -28,7 +29,7 @@ KERNEL_KINDS = ["mask_scan", "zero_ignored_rows", "logits_gemm", "softmax_grad",
 # Every symbol include/flce.h declares.
 EXPORTS = ["flce_chunk_size", "flce_chunk_size_mi355x", "flce_workspace_bytes", "flce_fwd_bwd",
            "flce_workspace_bytes_ex", "flce_workspace_row_index_offset", "flce_fwd_bwd_ex",
-           "flce_scale_cast", "flce_status_string", "flce_last_error",
+           "flce_fwd_bwd_ex_noalloc", "flce_scale_cast", "flce_status_string", "flce_last_error",
            "flce_profile_begin", "flce_profile_begin_kinds", "flce_profile_end",
            "flce_kernel_name"]
 
@@ -95,6 +96,10 @@ def load():
                                     P, P, P, P, SZ, P, ctypes.POINTER(FlceStats),
                                     ctypes.POINTER(FlceOptions)]
     lib.flce_fwd_bwd_ex.restype = I
+    lib.flce_fwd_bwd_ex_noalloc.argtypes = [P, P, P, I64, I64, I64, I, I64, I, I64, I32, I, I32,
+                                            I32, P, P, P, P, P, ctypes.POINTER(FlceStats),
+                                            ctypes.POINTER(FlceOptions)]
+    lib.flce_fwd_bwd_ex_noalloc.restype = I
     lib.flce_scale_cast.argtypes = [P, I, P, I, I64, P, P]
     lib.flce_scale_cast.restype = I
     lib.flce_status_string.argtypes = [I]
@@ -166,6 +171,19 @@ def flce_fwd_bwd_ex(X: int, W: int, targets: int, BT: int, H: int, V: int, dtype
                                   workspace_bytes, stream,
                                   ctypes.byref(stats) if stats is not None else None,
                                   ctypes.byref(opt) if opt is not None else None)
+
+
+def flce_fwd_bwd_ex_noalloc(X: int, W: int, targets: int, BT: int, H: int, V: int, dtype: int,
+                            ignore_index: int, reduction: int, chunk_size: int,
+                            chunk_mem_const: int, accum_dtype: int, frozen_weight: int,
+                            accumulate_dw: int, grad_output, loss: int, dX, dW, stream,
+                            stats: FlceStats | None = None, opt: FlceOptions | None = None) -> int:
+    return load().flce_fwd_bwd_ex_noalloc(X, W, targets, BT, H, V, dtype, ignore_index, reduction,
+                                          chunk_size, chunk_mem_const, accum_dtype,
+                                          frozen_weight, accumulate_dw, grad_output, loss, dX, dW,
+                                          stream,
+                                          ctypes.byref(stats) if stats is not None else None,
+                                          ctypes.byref(opt) if opt is not None else None)
 
 
 def flce_scale_cast(src: int, src_dtype: int, dst: int, dst_dtype: int, n: int, scale,

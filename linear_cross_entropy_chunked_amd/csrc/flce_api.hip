@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "flce.h"
@@ -201,8 +202,10 @@ struct ProfScope {
     if (e_ != hipSuccess) return fail_hip(e_, #expr); \
   } while (0)
 
-// Pinned host word pair for the single device-to-host read.
+// Pinned host word pair for the single device-to-host read, and a plain one
+// for the entry point that allocates nothing.
 thread_local ScanFlags* g_host_flags = nullptr;
+thread_local ScanFlags g_pageable_flags;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -356,13 +359,16 @@ int flce_scale_cast(const void* src, flce_dtype_t src_dtype, void* dst, flce_dty
 
 namespace {
 
-// The whole call.
+// The whole call.  `pageable_flags`: read the labelled-row count and the
+// range flag at the single sync into plain host memory instead of the
+// thread's pinned pair (which is allocated on its first use), so that the
+// call allocates nothing.
 int fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
             int64_t V, flce_dtype_t dtype, int64_t ignore_index, flce_reduction_t reduction,
             int64_t chunk_size, int32_t chunk_mem_const, flce_dtype_t accum_dtype,
             int32_t frozen_weight, int32_t accumulate_dw, const float* grad_output, float* loss,
             void* dX, void* dW, void* workspace, size_t workspace_bytes, void* stream,
-            flce_stats_t* stats, const flce_options_t* opt) {
+            flce_stats_t* stats, const flce_options_t* opt, bool pageable_flags) {
   // ---- host-side checks: nothing is launched or written on failure
   if (dtype < FLCE_F32 || dtype > FLCE_BF16) return FLCE_E_DTYPE;
   if (accum_dtype != dtype && accum_dtype != FLCE_F32) return FLCE_E_DTYPE;
@@ -475,15 +481,18 @@ int fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, in
     io.acc_none = none ? o.accuracy : nullptr;
     io.pred = o.predicted;
     FLCE_LAUNCH(FLCE_K_ZERO_ROWS, launch_zero_ignored(targets, BT, H, ignore_index, io, st));
-    if (!g_host_flags) {
-      hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&g_host_flags), 64,
-                                   hipHostMallocDefault);
-      if (e != hipSuccess) {
-        g_host_flags = nullptr;
-        return fail_hip(e, "hipHostMalloc");
+    ScanFlags* hf = &g_pageable_flags;
+    if (!pageable_flags) {
+      if (!g_host_flags) {
+        hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&g_host_flags), 64,
+                                     hipHostMallocDefault);
+        if (e != hipSuccess) {
+          g_host_flags = nullptr;
+          return fail_hip(e, "hipHostMalloc");
+        }
       }
+      hf = g_host_flags;
     }
-    ScanFlags* hf = g_host_flags;
     hipError_t e = hipMemcpyAsync(hf, dflags, sizeof(ScanFlags), hipMemcpyDeviceToHost, st);
     if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(flags)");
     e = hipStreamSynchronize(st);
@@ -665,6 +674,57 @@ int fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, in
 
 }  // namespace
 
+// ------------------------------------------------------------ static scratch
+// Device memory of flce_fwd_bwd_ex_noalloc: the workspace of callers that
+// cannot allocate.  One copy per GPU, at its own address, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device memory: kernels and copies get the address from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[FLCE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch; the stream must run on
+// that device.
+int scratch_for(hipStream_t st, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (st) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(st, &sdev);
+    if (e != hipSuccess) return fail_hip(e, "hipStreamGetDevice");
+    if ((int)sdev != dev) {
+      std::snprintf(g_last_error, sizeof g_last_error,
+                    "flce_fwd_bwd_ex_noalloc: the stream runs on device %d, the current device "
+                    "is %d",
+                    (int)sdev, dev);
+      return FLCE_E_ARG;
+    }
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) {
+    std::snprintf(g_last_error, sizeof g_last_error,
+                  "flce_fwd_bwd_ex_noalloc: device ordinal %d beyond %d", dev,
+                  kMaxScratchDevices - 1);
+    return FLCE_E_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FLCE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
@@ -676,7 +736,34 @@ int flce_fwd_bwd_ex(const void* X, const void* W, const int64_t* targets, int64_
                     const flce_options_t* opt) {
   return fwd_bwd(X, W, targets, BT, H, V, dtype, ignore_index, reduction, chunk_size,
                  chunk_mem_const, accum_dtype, frozen_weight, accumulate_dw, grad_output, loss, dX,
-                 dW, workspace, workspace_bytes, stream, stats, opt);
+                 dW, workspace, workspace_bytes, stream, stats, opt, false);
+}
+
+int flce_fwd_bwd_ex_noalloc(const void* X, const void* W, const int64_t* targets, int64_t BT,
+                            int64_t H, int64_t V, flce_dtype_t dtype, int64_t ignore_index,
+                            flce_reduction_t reduction, int64_t chunk_size,
+                            int32_t chunk_mem_const, flce_dtype_t accum_dtype,
+                            int32_t frozen_weight, int32_t accumulate_dw,
+                            const float* grad_output, float* loss, void* dX, void* dW,
+                            void* stream, flce_stats_t* stats, const flce_options_t* opt) {
+  if (dtype < FLCE_F32 || dtype > FLCE_BF16) return FLCE_E_DTYPE;
+  const size_t need =
+      flce_workspace_bytes_ex(BT, H, V, dtype, chunk_size, chunk_mem_const, opt);
+  if (need == 0) return FLCE_E_ARG;
+  if (need > (size_t)FLCE_SCRATCH_BYTES) {
+    std::snprintf(g_last_error, sizeof g_last_error,
+                  "flce_fwd_bwd_ex_noalloc: this call needs %zu bytes of workspace, the static "
+                  "scratch holds %zu; use a smaller chunk_size or flce_fwd_bwd_ex",
+                  need, (size_t)FLCE_SCRATCH_BYTES);
+    return FLCE_E_WORKSPACE;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  const int rc = scratch_for(st, &ws);
+  if (rc != FLCE_OK) return rc;
+  return fwd_bwd(X, W, targets, BT, H, V, dtype, ignore_index, reduction, chunk_size,
+                 chunk_mem_const, accum_dtype, frozen_weight, accumulate_dw, grad_output, loss, dX,
+                 dW, ws, (size_t)FLCE_SCRATCH_BYTES, stream, stats, opt, true);
 }
 
 int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H,
@@ -687,7 +774,7 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
                  void* stream, flce_stats_t* stats) {
   return fwd_bwd(X, W, targets, BT, H, V, dtype, ignore_index, reduction, chunk_size,
                  chunk_mem_const, accum_dtype, frozen_weight, accumulate_dw, grad_output, loss, dX,
-                 dW, workspace, workspace_bytes, stream, stats, nullptr);
+                 dW, workspace, workspace_bytes, stream, stats, nullptr, false);
 }
 
 }  // extern "C"

@@ -187,6 +187,21 @@ def test_size_limits_on_host(flce_lib, kw, status):
     assert flce_lib.flce_fwd_bwd(**a) == status
 
 
+def test_noalloc_rejects_oversized_calls_on_host(flce_lib):
+    """The no-allocation entry point refuses, before any HIP call, a call
+    whose workspace would not fit its static scratch, and bad dtypes."""
+    a = dict(FAR, BT=8192, H=4096, V=128256, dtype=flce_lib.BF16, ignore_index=-100,
+             reduction=0, chunk_size=2048, chunk_mem_const=1, accum_dtype=flce_lib.F32,
+             frozen_weight=0, accumulate_dw=0, grad_output=None, stream=None)
+    a.pop("workspace")
+    assert flce_lib.flce_workspace_bytes(8192, 4096, 128256, flce_lib.BF16, 2048, 1) > \
+        flce_lib.SCRATCH_BYTES
+    assert flce_lib.flce_fwd_bwd_ex_noalloc(**a) == -4
+    assert "static scratch" in flce_lib.flce_last_error()
+    assert flce_lib.flce_fwd_bwd_ex_noalloc(**dict(a, dtype=7)) == -2
+    assert flce_lib.flce_fwd_bwd_ex_noalloc(**dict(a, H=0)) == -1
+
+
 def test_row_index_offset(flce_lib):
     """The labelled-row index sits 256-byte aligned inside the workspace, with
     room for BT int32 entries, for every option set."""
