@@ -70,13 +70,23 @@ WORKLOADS = {
 }
 
 
+# Measured with the headline workload by default: the 256-row chunk of the
+# same shape, the ignored-token speed-up at each labelled share (trained
+# weight; PR #1554, Summary: about 1 / labelled share faster), the 256-row
+# chunk at BT 8192 and 32768 (PR #1439, Details: the 256-row slab is flat in
+# BT), and the fp32 same-dtype sweep (issue #1323, comparison table).
+DEFAULT_EXTRA = ["llama3_8b_lm_head_c256", "masked_sft_100_trained", "masked_sft_75_trained",
+                 "masked_sft_50_trained", "masked_sft_10_trained", "long_seq_8k_c256",
+                 "long_seq_32k_c256", "same_dtype_sweep_f32"]
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="llama3_8b_lm_head", choices=sorted(WORKLOADS))
-    p.add_argument("--extra", default="llama3_8b_lm_head_c256",
+    p.add_argument("--extra", default=",".join(DEFAULT_EXTRA),
                    help="comma-separated extra workloads reported under 'extra' ('' for none)")
     p.add_argument("--cpu-rows", type=int, default=256, help="rows in the oracle's timed sample")
     p.add_argument("--chunk-sweep", default="",
@@ -105,6 +115,9 @@ def parse():
     p.add_argument("--summarize-profile", nargs="+", metavar="CSV",
                    help="print a text summary of rocprofv3 csv output (kernel stats, or "
                         "FETCH_SIZE / WRITE_SIZE counter collections) and exit")
+    p.add_argument("--rates", metavar="JSON",
+                   help="with --summarize-profile: also tabulate the per-kernel achieved "
+                        "rates from the bench JSON line the profiled run printed")
     return p.parse_args()
 
 
@@ -112,23 +125,40 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+_HOST = {}
+
+
 def make_inputs(cfg, dev):
-    import torch
+    """Seeded host inputs of a workload and their device copies.  X, W and the
+    targets are cached separately on the host (workloads that differ only in
+    BT, the labelled share or the chunk size share them), only the last
+    workload's device copies are kept."""
     import synthetic_inputs as si
-    BT, H, V = cfg["BT"], cfg["H"], cfg["V"]
-    log(f"generating inputs BT={BT} H={H} V={V} {cfg['dtype']}")
+    BT, H, V, dt, seed = cfg["BT"], cfg["H"], cfg["V"], cfg["dtype"], cfg["seed"]
     t0 = time.perf_counter()
-    X = si.make_x(BT, H, cfg["dtype"], cfg["seed"])
-    W = si.make_w(V, H, cfg["dtype"], cfg["seed"])
-    share = cfg["share"]
-    if share >= 1.0:
-        t = si.make_targets(BT, V, cfg["seed"])
-    else:
-        t = si.make_targets(BT, V, cfg["seed"], ignore="prompt_first", frac=1.0 - share,
-                            seq_len=cfg.get("seq_len", BT))
-    host = (X, W, t)
+    kx, kw = ("X", BT, H, dt, seed), ("W", V, H, dt, seed)
+    kt = ("t", BT, V, seed, cfg["share"], cfg.get("seq_len", BT))
+    keep = {kx, kw, kt}
+    for k in [k for k in _HOST if k not in keep and k[0] != "W"]:
+        del _HOST[k]
+    if kx not in _HOST:
+        log(f"generating X [{BT}, {H}] {dt}")
+        _HOST[kx] = si.make_x(BT, H, dt, seed)
+    if kw not in _HOST:
+        for k in [k for k in _HOST if k[0] == "W"]:
+            del _HOST[k]
+        log(f"generating W [{V}, {H}] {dt}")
+        _HOST[kw] = si.make_w(V, H, dt, seed)
+    if kt not in _HOST:
+        share = cfg["share"]
+        if share >= 1.0:
+            _HOST[kt] = si.make_targets(BT, V, seed)
+        else:
+            _HOST[kt] = si.make_targets(BT, V, seed, ignore="prompt_first", frac=1.0 - share,
+                                        seq_len=cfg.get("seq_len", BT))
+    host = (_HOST[kx], _HOST[kw], _HOST[kt])
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
-    return host, (X.to(dev), W.to(dev), t.to(dev))
+    return host, tuple(h.to(dev) for h in host)
 
 
 def prepare(cfg, dev, host_dev=None):
@@ -254,28 +284,96 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None, sensor_s=0.0):
     return res, host
 
 
+def kernel_work(kind, res, cfg):
+    """Algorithmic work of one average launch of a kernel kind: (flops, HBM bytes).
+
+    Per chunk of r labelled rows (r = n_valid / chunks_run on average),
+    s = operand itemsize, a = grad_weight itemsize:
+      logits_gemm   2 r H V flops; W V H s + rows r H s + slab r V s
+      softmax_grad  slab read + write 2 r V s (+ the block maxima, 8 r V / 64)
+      dx_gemm       2 r H V flops; W V H s + G r V s + dX rows r H s
+      dx_reduce     split partials S r H 4 + dX rows r H s
+      dw_gemm       2 r H V flops; G r V s + gathered rows r H s + dW written
+                    once per call and read-modified-written by the later chunks
+      gather_rows   X rows r H s read + the transposed copy r H s written
+      mask_scan     targets 8 BT + row index 4 n_valid
+      zero_ignored_rows  dX rows of the ignored rows (BT - n_valid) H s
+      loss_finalize per-row losses 4 n_valid
+    """
+    H, V, BT = res["H"], res["V"], res["BT"]
+    n, chunks = res["n_valid"], max(res["chunks_run"], 1)
+    r = n / chunks
+    s = 4 if cfg["dtype"] == "f32" else 2
+    a = 4 if cfg["accum"] == "f32" else s
+    if kind == "logits_gemm":
+        return 2.0 * r * H * V, V * H * s + r * H * s + r * V * s
+    if kind == "softmax_grad":
+        return 0.0, 2.0 * r * V * s + 8.0 * r * V / 64
+    if kind == "dx_gemm":
+        return 2.0 * r * H * V, V * H * s + r * V * s + r * H * s
+    if kind == "dx_reduce":
+        return 0.0, res["dx_splits"] * r * H * 4 + r * H * s
+    if kind == "dw_gemm":
+        return 2.0 * r * H * V, r * V * s + r * H * s + V * H * a * (2.0 * chunks - 1) / chunks
+    if kind == "gather_rows":
+        return 0.0, 2.0 * r * H * s
+    if kind == "mask_scan":
+        return 0.0, 8.0 * BT + 4.0 * n
+    if kind == "zero_ignored_rows":
+        return 0.0, (BT - n) * H * s
+    if kind == "loss_finalize":
+        return 0.0, 4.0 * n
+    return None
+
+
+def kernel_rates(res, cfg):
+    """Achieved rate of every kernel kind of a step against MI355X peak, from
+    the per-kernel event table: HBM GB/s for all, MFMA TFLOP/s for the GEMMs,
+    and which of the two rooflines bounds the kernel."""
+    out = {}
+    for kind, k in res["kernels"].items():
+        w = kernel_work(kind, res, cfg)
+        if w is None or not k["ms_per_launch"]:
+            continue
+        flops, byts = w
+        sec = k["ms_per_launch"] * 1e-3
+        e = dict(us_per_launch=k["ms_per_launch"] * 1e3, launches_per_step=k["launches"],
+                 hbm_gbs=byts / sec / 1e9, hbm_frac=byts / sec / 1e9 / HBM_PEAK_GBS,
+                 algorithmic_bytes=byts)
+        if flops:
+            peak = MFMA_PEAK_TFLOPS[cfg["dtype"]]
+            e.update(tflops=flops / sec / 1e12, mfma_frac=flops / sec / 1e12 / peak,
+                     algorithmic_flops=flops)
+            e["bound"] = "mfma" if flops / (peak * 1e12) >= byts / (HBM_PEAK_GBS * 1e9) else "hbm"
+        else:
+            e["bound"] = "hbm"
+        out[kind] = e
+    return out
+
+
 def roofline(res, cfg):
-    """Roofline figures of the dominant kernel of one step, timed in the timed steps."""
-    c, H, V = res["chunk_size"], res["H"], res["V"]
+    """Roofline figures of the dominant kernel of one step, timed in the timed
+    steps: against the MFMA peak when its algorithmic flops take longer at peak
+    than its algorithmic bytes at 8 TB/s, else against HBM bandwidth."""
     k = res["timed_kernel"]
     name = k["name"]
-    s = 4 if cfg["dtype"] == "f32" else 2
-    if name in ("logits_gemm", "dx_gemm", "dw_gemm"):
-        # per launch: one full chunk of c rows -> 2 c H V flops
-        rows = min(c, res["n_valid"])
-        work = 2.0 * rows * H * V
-        achieved = work / (k["ms_per_launch"] * 1e-3) / 1e12
-        peak = MFMA_PEAK_TFLOPS[cfg["dtype"]]
-        return dict(kernel=name, bound="mfma", achieved=achieved, peak=peak, unit="TFLOP/s",
-                    frac=achieved / peak, traffic=None,
-                    work_per_launch=f"2*c*H*V flops = {work:.4g} (c={rows})")
-    # bandwidth-bound kernels: softmax reads + writes the slab once
-    rows = min(c, res["n_valid"])
-    byts = 2.0 * rows * V * s
-    achieved = byts / (k["ms_per_launch"] * 1e-3) / 1e9
-    return dict(kernel=name, bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=achieved / HBM_PEAK_GBS, traffic=None,
-                work_per_launch=f"2*c*V*itemsize bytes = {byts:.4g}")
+    flops, byts = kernel_work(name, res, cfg)
+    sec = k["ms_per_launch"] * 1e-3
+    rows = res["n_valid"] / max(res["chunks_run"], 1)
+    peak_f = MFMA_PEAK_TFLOPS[cfg["dtype"]]
+    if flops and flops / (peak_f * 1e12) >= byts / (HBM_PEAK_GBS * 1e9):
+        achieved = flops / sec / 1e12
+        return dict(kernel=name, bound="mfma", achieved=achieved, peak=peak_f, unit="TFLOP/s",
+                    frac=achieved / peak_f, traffic=None,
+                    hbm_frac_of_algorithmic_bytes=byts / sec / 1e9 / HBM_PEAK_GBS,
+                    work_per_launch=f"2*c*H*V flops = {flops:.4g} (c={rows:g} rows on average)")
+    achieved = byts / sec / 1e9
+    out = dict(kernel=name, bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+               frac=achieved / HBM_PEAK_GBS, traffic=None,
+               work_per_launch=f"algorithmic bytes = {byts:.4g} (c={rows:g} rows on average)")
+    if flops:
+        out["mfma_frac"] = flops / sec / 1e12 / peak_f
+    return out
 
 
 def cpu_baseline(host, cfg, rows):
@@ -446,6 +544,25 @@ def summarize_profile(paths):
             print(f"{'kernel':70s} {'counter':12s} {'dispatches':>10s} {'avg_per_dispatch':>18s}")
             for (k, c), v in sorted(agg.items()):
                 print(f"{k:70s} {c:12s} {len(v):10d} {sum(v)/len(v):18.1f}")
+        print()
+
+
+def summarize_rates(path):
+    """Per-kernel achieved rates (HIP events in the profiled run) of every
+    workload in a bench JSON line, against MI355X peak."""
+    line = [l for l in open(path) if l.startswith("{")][-1]
+    out = json.loads(line)
+    runs = [(out["config"]["workload"], out["detail"])] + list(out.get("extra", {}).items())
+    for name, res in runs:
+        print(f"## achieved rates, {name}: chunk {res['chunk_size']}, {res['chunks_run']} "
+              f"chunks, {res['n_valid']} labelled rows, {res['ms_per_step']:.3f} ms per step")
+        print(f"{'kernel':18s} {'launches':>8s} {'us/launch':>10s} {'bound':>5s} "
+              f"{'GB/s':>9s} {'of 8 TB/s':>9s} {'TFLOP/s':>9s} {'of peak':>8s}")
+        for k, e in sorted(res.get("kernel_rates", {}).items(),
+                           key=lambda kv: -kv[1]["us_per_launch"] * kv[1]["launches_per_step"]):
+            tf = f"{e['tflops']:9.1f} {100 * e['mfma_frac']:7.1f}%" if "tflops" in e else ""
+            print(f"{k:18s} {e['launches_per_step']:8d} {e['us_per_launch']:10.2f} "
+                  f"{e['bound']:>5s} {e['hbm_gbs']:9.1f} {100 * e['hbm_frac']:8.1f}% {tf}")
         print()
 
 
@@ -674,6 +791,40 @@ def chunk_sweep(a, cfg, dev):
           flush=True)
 
 
+def extra_summaries(extras):
+    """What the extra workloads show together: the ignored-token speed-up
+    against 1 / labelled share (PR #1554, Summary), and the transient memory of
+    a 256-row chunk at two sequence lengths (PR #1439, Details)."""
+    out = {}
+    base = extras.get("masked_sft_100_trained")
+    if base:
+        rows = []
+        for sh in (0.75, 0.5, 0.1):
+            e = extras.get(f"masked_sft_{int(sh * 100)}_trained")
+            if e:
+                rows.append(dict(labelled_share=sh, n_valid=e["n_valid"],
+                                 chunks_run=e["chunks_run"], ms_per_step=e["ms_per_step"],
+                                 speedup=base["ms_per_step"] / e["ms_per_step"],
+                                 ideal_1_over_share=base["n_valid"] / e["n_valid"],
+                                 chunk_ratio=base["chunks_run"] / e["chunks_run"]))
+        out["ignored_token_speedup"] = dict(baseline_ms=base["ms_per_step"], rows=rows)
+    a, b = extras.get("long_seq_8k_c256"), extras.get("long_seq_32k_c256")
+    if a and b:
+        out["flat_transient_c256"] = dict(
+            bt_8192_peak_bytes=a["peak_transient_bytes"],
+            bt_32768_peak_bytes=b["peak_transient_bytes"],
+            bt_8192_workspace_bytes=a["workspace_bytes"],
+            bt_32768_workspace_bytes=b["workspace_bytes"],
+            workspace_difference_bytes=b["workspace_bytes"] - a["workspace_bytes"],
+            row_index_and_loss_bytes=8 * (b["BT"] - a["BT"]),
+            note="peak = max_memory_allocated - memory_allocated around a call whose workspace "
+                 "is allocated inside the window (torch rounds that allocation up to 2 MiB); "
+                 "the [256, V] slab and the other chunk buffers are the same at both BT, and "
+                 "the workspace grows only by the int32 row index and fp32 per-row loss "
+                 "(8 B per row)")
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -682,6 +833,8 @@ def main():
         sys.exit(2)
     if a.summarize_profile:
         summarize_profile(a.summarize_profile)
+        if a.rates:
+            summarize_rates(a.rates)
         return
     if a.record_traffic:
         record_traffic(*a.record_traffic)
@@ -703,18 +856,26 @@ def main():
     if a.autograd:
         autograd_bench(a, cfg, dev)
         return
+    t_start = time.perf_counter()
     main_res, host = run_workload(a.workload, cfg, a.steps, a.warmup, dev,
                                   sensor_s=a.sensor_seconds)
+    main_res["kernel_rates"] = kernel_rates(main_res, cfg)
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(host, cfg, a.cpu_rows)
+    del host
     extras = {}
     for name in [e for e in a.extra.split(",") if e and e != a.workload]:
         ecfg = WORKLOADS[name]
-        same = all(ecfg[k] == cfg[k] for k in ("BT", "H", "V", "dtype", "seed", "share"))
-        hd = None
-        if same:
-            X, W, t = host
-            hd = (host, (X.to(dev), W.to(dev), t.to(dev)))
-        extras[name], _ = run_workload(name, ecfg, max(a.steps // 2, 2), a.warmup, dev, hd,
-                                       sensor_s=a.sensor_seconds)
+        res, _ = run_workload(name, ecfg, max(a.steps // 2, 2), a.warmup, dev,
+                              sensor_s=a.sensor_seconds)
+        erl = roofline(res, ecfg)
+        erl["traffic"] = recorded_traffic(erl["kernel"], name)
+        res["roofline"] = erl
+        res["kernel_rates"] = kernel_rates(res, ecfg)
+        extras[name] = res
+        torch.cuda.empty_cache()
+    summaries = extra_summaries(extras)
     rl = roofline(main_res, cfg)
     rl["traffic"] = recorded_traffic(rl["kernel"], a.workload)
     sens = main_res["gpu_sensors"]
@@ -746,10 +907,12 @@ def main():
         "algorithmic_tflops": main_res["algorithmic_tflops"],
         "roofline": rl,
     }
-    if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(host, cfg, a.cpu_rows)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     out["detail"] = main_res
+    out["summaries"] = summaries
     out["extra"] = extras
+    out["wall_s"] = time.perf_counter() - t_start
     out["context"] = ("pages' figures on other hardware (not targets): BT 8192, H 4096, "
                       "V 128256 bf16 on H200, chunk 256: 53.039 ms; chunk 2048: 37.748 ms")
     print(json.dumps(out), flush=True)

@@ -100,12 +100,26 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int dtype, int64_t c, const
   L.ldx = round_up(c, 8);
   L.stats_ld = ceil_div(V, stats_cols());
   const DxTile dt = dx_tile(dtype, (int)c, H);
+  // grad_input split over V: s splits make tiles x s workgroups, each with
+  // 1/s of the work, run in ceil(tiles x s / slots) rounds.  Take the s that
+  // minimises rounds / s (the time in units of one unsplit workgroup), moving
+  // to a larger s only for a gain above 3 %: every split adds c x H fp32
+  // partials to write and reduce.  (Rounding s up to cover the chip, as
+  // tiles x s >= slots, can leave a nearly empty last round: 21 tiles x 13
+  // splits = 273 workgroups on 256 CUs take two rounds.)
   const int64_t tiles = ceil_div(c, dt.bm) * ceil_div(H, dt.bn);
-  int64_t splits = ceil_div((int64_t)kDxCUs * dt.wgs, tiles);
-  const int64_t by_k = L.ldz / kDxMinKPerSplit;
-  if (splits > by_k) splits = by_k;
-  if (splits > kDxMaxSplits) splits = kDxMaxSplits;
-  if (splits < 1) splits = 1;
+  const int64_t slots = (int64_t)kDxCUs * dt.wgs;
+  int64_t smax = L.ldz / kDxMinKPerSplit;
+  if (smax > kDxMaxSplits) smax = kDxMaxSplits;
+  int64_t splits = 1;
+  double best = (double)ceil_div(tiles, slots);
+  for (int64_t sp = 2; sp <= smax; ++sp) {
+    const double t = (double)ceil_div(tiles * sp, slots) / (double)sp;
+    if (t < best * 0.97) {
+      best = t;
+      splits = sp;
+    }
+  }
   L.k_per_split = round_up(ceil_div(L.ldz, splits), 64);
   L.splits = (int)ceil_div(L.ldz, L.k_per_split);
   size_t off = 0;
