@@ -129,7 +129,8 @@ def test_ragged_large_tiles(pkg, dtype, accum):
 
 @pytest.mark.parametrize("dtype,shape", [("bf16", (300, 256, 1000, 64)), ("bf16", (900, 392, 1100, 512)),
                                          ("f16", (900, 392, 1100, 512)), ("f32", (900, 392, 1100, 512)),
-                                         ("f32", (300, 256, 1000, 64))])
+                                         ("f32", (300, 256, 1000, 64)), ("bf16", (300, 64, 20001, 128)),
+                                         ("f32", (300, 64, 20001, 64))])
 def test_repeated_calls_are_bit_identical(pkg, dtype, shape):
     """Every tile path (128x128; eight-wave 256x256 for 16-bit operands;
     four-wave 256x256 for fp32) gives bit-identical loss, dX and dW on repeated
@@ -143,6 +144,43 @@ def test_repeated_calls_are_bit_identical(pkg, dtype, shape):
         assert torch.equal(r.loss, runs[0].loss)
         assert torch.equal(r.dX, runs[0].dX)
         assert torch.equal(r.dW, runs[0].dW)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_streaming_logits_path(pkg, dtype, chunk):
+    """Chunks of at most 128 rows with a vocabulary of 16384 or more take the
+    logits tile that keeps seven W tiles in flight (one workgroup per CU);
+    ragged V and several chunks, a ragged last one included."""
+    BT, H, V = 330, 72, 20001
+    X, W, t = si.make_case(BT, H, V, dtype, 4100 + chunk, ignore="scattered", frac=0.15)
+    r = _run(pkg, X, W, t, reduction="mean", chunk_size=chunk, accum_dtype=torch.float32)
+    ref = oracle.flce(X, W, t, reduction="mean")
+    assert r.stats["chunk_size"] == chunk and r.stats["n_valid"] == ref["n_valid"]
+    _check(r, ref, dtype, "mean")
+
+
+def test_streaming_logits_path_with_options(pkg):
+    """The same tile with a bias, the z-loss and the predicted token."""
+    BT, H, V = 200, 64, 17000
+    X, W, t = si.make_case(BT, H, V, "bf16", 4200, ignore="scattered", frac=0.2)
+    b = (si.make_x(1, V, "f32", 4207).reshape(-1) * 0.5).to(torch.bfloat16)
+    dev = torch.device("cuda:0")
+    r = pkg.fused_linear_cross_entropy_fwd_bwd(
+        X.to(dev), W.to(dev), t.to(dev), bias=b.to(dev), reduction="sum", chunk_size=128,
+        accum_dtype=torch.float32, z_loss_scale=1e-3, return_predicted=True)
+    torch.cuda.synchronize()
+    ref = oracle.flce_ex(X, W, t, bias=b, z_loss_scale=1e-3, reduction="sum")
+    assert abs(float(r.loss) - ref["loss"]) <= 2e-3 * abs(ref["loss"])
+    assert _rel(r.dX, ref["dX"]) <= 2e-2 and _rel(r.dW, ref["dW"]) <= 2e-2
+    assert _rel(r.grad_bias, ref["grad_bias"]) <= 2e-2
+    pred = r.predicted.cpu().numpy()
+    lab = (t != -100).numpy()
+    assert np.all(pred[~lab] == -1)
+    z = oracle.widen(X) @ oracle.widen(W).T + oracle.widen(b)[None, :]
+    zs = np.sort(z, axis=1)
+    clear = lab & (zs[:, -1] - zs[:, -2] > 1e-4 * np.abs(z).max(axis=1))
+    np.testing.assert_array_equal(pred[clear], ref["predicted"][clear])
 
 
 def test_split_grad_input_path(pkg):
