@@ -4,15 +4,18 @@ One step = one flce_fwd_bwd call over one batch (row compaction, the chunk
 loop of logits GEMM -> softmax-gradient -> grad_input GEMM -> grad_weight
 GEMM, loss reduction).  Default workload: the Llama-3-8B lm_head shape,
 bf16, BT 8192, H 4096, V 128256, all rows labelled, mean, fp32 grad_weight,
-chunk_size 2048; the 256-row chunk geometry is measured too and reported
-under "extra".  Inputs are seeded synthetic tensors already resident in HBM
+chunk_size 2048.  Reported under "extra": the 256-row chunk of that shape,
+masked SFT at labelled shares 100/75/50/10 %, the long-sequence shape at
+chunk 256 for BT 8192 and 32768, and the fp32 same-dtype sweep.  Inputs are seeded synthetic tensors already resident in HBM
 when the timed region starts.
 
 Prints one JSON line.  ``value`` = tokens/s of the whole job (BT x steps /
 elapsed).  ``roofline`` is for the dominant kernel, with its average launch
 duration measured by HIP events on the stream it runs on, over the timed
-steps; only that kernel is bracketed by events there, and the per-kernel
-table in ``detail`` comes from further steps with every kernel bracketed.
+steps; only that kernel is bracketed by events there.  The same steps are
+also run with no kernel events (``ms_per_step_unbracketed``: each pair of
+events costs about 12 us of stream time), and with every kernel bracketed
+for the per-kernel table in ``detail``.
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of rows of
 the same workload on the host cores.
 """
@@ -212,11 +215,13 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None, sensor_s=0.0):
         p.call(ws)
 
     log(f"{name}: {warmup} warmup step(s)")
-    # The warmup is profiled to find the kernel that dominates a step.  The timed
-    # steps then bracket only that kernel with HIP events (each pair of events
-    # adds a few microseconds to the stream; bracketing every kernel cost 0.6 %
-    # of a chunk-2048 step and 2.6 % of a chunk-256 one), and a second run of
-    # the same steps right after brackets every kernel for the per-kernel table.
+    # The warmup is profiled to find the kernel that dominates a step.  The
+    # timed steps bracket only that kernel with HIP events, for its launch
+    # duration.  Each pair of events adds about 12 us of stream time (at 64
+    # chunks that is 0.8 ms per step for one kernel kind, 4 ms for all six),
+    # so the same steps are also run with no kernel events at all
+    # (ms_per_step_unbracketed), and once more with every kernel bracketed for
+    # the per-kernel table.
     pkg.flce_profile_begin()
     for _ in range(warmup):
         step()
@@ -238,6 +243,13 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None, sensor_s=0.0):
     step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     pct = lambda q: step_ms[min(len(step_ms) - 1, int(round(q * (len(step_ms) - 1))))]
     tprof = pkg.flce_profile_end()[dominant]
+    log(f"{name}: {steps} step(s) with no kernel events")
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    plain_ms = ev[0].elapsed_time(ev[1]) / steps
     log(f"{name}: {steps} step(s) with every kernel bracketed")
     pkg.flce_profile_begin()
     t1 = time.perf_counter()
@@ -267,13 +279,16 @@ def run_workload(name, cfg, steps, warmup, dev, host_dev=None, sensor_s=0.0):
         reduction=cfg["reduction"], frozen_weight=frozen, labelled_share=cfg["share"],
         seq_len=cfg.get("seq_len", BT), chunk_size=st.chunk_size, chunks_run=st.chunks_run, dx_splits=st.dx_splits,
         n_valid=n_lab, ms_per_step=ms, tokens_per_s=BT * steps / elapsed,
+        ms_per_step_unbracketed=plain_ms,
         step_ms_p20_p50_p80=[pct(0.2), pct(0.5), pct(0.8)],
         algorithmic_tflops=flops / (ms * 1e-3) / 1e12,
         mfma_frac=flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[cfg["dtype"]],
         workspace_bytes=wsb, peak_transient_bytes=int(peak_transient),
         timed_kernel=dict(name=dominant, launches=tprof[0] // steps,
                           ms_per_launch=(tprof[1] / tprof[0] if tprof[0] else 0.0),
-                          ms_per_step=tprof[1] / steps),
+                          ms_per_step=tprof[1] / steps,
+                          measured_in=f"{steps} steps right after the timed ones, with HIP events "
+                                f"around this kernel only"),
         kernels={k: dict(launches=v[0] // steps, ms_per_launch=(v[1] / v[0] if v[0] else 0.0),
                          ms_per_step=v[1] / steps)
                  for k, v in prof.items() if v[0]},
@@ -803,11 +818,15 @@ def extra_summaries(extras):
             e = extras.get(f"masked_sft_{int(sh * 100)}_trained")
             if e:
                 rows.append(dict(labelled_share=sh, n_valid=e["n_valid"],
-                                 chunks_run=e["chunks_run"], ms_per_step=e["ms_per_step"],
-                                 speedup=base["ms_per_step"] / e["ms_per_step"],
+                                 chunks_run=e["chunks_run"],
+                                 ms_per_step=e["ms_per_step_unbracketed"],
+                                 speedup=base["ms_per_step_unbracketed"]
+                                 / e["ms_per_step_unbracketed"],
                                  ideal_1_over_share=base["n_valid"] / e["n_valid"],
                                  chunk_ratio=base["chunks_run"] / e["chunks_run"]))
-        out["ignored_token_speedup"] = dict(baseline_ms=base["ms_per_step"], rows=rows)
+        out["ignored_token_speedup"] = dict(
+            baseline_ms=base["ms_per_step_unbracketed"], rows=rows,
+            timing="steps with no per-kernel events (ms_per_step_unbracketed)")
     a, b = extras.get("long_seq_8k_c256"), extras.get("long_seq_32k_c256")
     if a and b:
         out["flat_transient_c256"] = dict(

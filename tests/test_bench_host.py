@@ -58,7 +58,7 @@ def test_kernel_rates_cover_every_timed_kind():
 
 def test_extra_summaries():
     import bench
-    e = {f"masked_sft_{p}_trained": dict(ms_per_step=40.0 * n / 8192, n_valid=n,
+    e = {f"masked_sft_{p}_trained": dict(ms_per_step_unbracketed=40.0 * n / 8192, n_valid=n,
                                          chunks_run=-(-n // 128))
          for p, n in ((100, 8192), (75, 6144), (50, 4096), (10, 819))}
     e["long_seq_8k_c256"] = dict(BT=8192, peak_transient_bytes=1 << 21, workspace_bytes=1000)
