@@ -595,7 +595,8 @@ def record_traffic(kernel, workload, fetch_csv, write_csv):
     that copy), taken from the --copy-calibration dispatches of the same run.
     """
     names = {"logits_gemm": "logits_kernel", "dx_gemm": "dx_kernel", "dw_gemm": "dw_kernel",
-             "softmax_grad": "softmax_kernel"}
+             "softmax_grad": "softmax_kernel", "gather_rows": "gather_t_kernel",
+             "mask_scan": "mask_scan_kernel", "dx_reduce": "dx_reduce_kernel"}
     kname = names[kernel]
     copy_f = [v for v in _per_dispatch(fetch_csv, lambda n: "copyBuffer" in n) if v > 1e5]
     copy_w = [v for v in _per_dispatch(write_csv, lambda n: "copyBuffer" in n) if v > 1e5]
