@@ -651,7 +651,7 @@ constexpr int kLogitsGroupM = 4, kDxGroupM = 4, kDwGroupN = 8;
 // Logits: slab[m, n] = X[idx[m], :] . W[n, :], plus per-(row, wave column
 // block) running max and sum of exp, and the target logit in fp32.
 // ---------------------------------------------------------------------------
-template <class T, class C, bool RANGE>
+template <class T, class C>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(LogitsArgs a) {
   typedef typename T::storage S;
   typedef DmaRows<T, C, C::BM> OA;
@@ -660,35 +660,27 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
   typedef Smem<C, OA, OB, PI::SA, PI::SB, C::BM * sizeof(int64_t)> SM;
   extern __shared__ __align__(16) unsigned char smem_raw[];
 
-  // The block's columns: one tile, or (cols_per_block > 0, one row tile) a
-  // contiguous range of whole 64-column blocks, walked a tile at a time.
-  int m0;
-  int64_t n_beg, n_end;
-  if (RANGE) {
-    m0 = 0;
-    n_beg = (int64_t)blockIdx.x * a.cols_per_block;
-    n_end = n_beg + a.cols_per_block < a.V ? n_beg + a.cols_per_block : a.V;
-  } else {
-    const int tiles_m = (a.rows + C::BM - 1) / C::BM;
-    const int tiles_n = (int)((a.V + C::BN - 1) / C::BN);
-    const int lin = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-    int tm, tn;  // M fastest within a group: blocks sharing a W tile are adjacent
-    grouped_tile(lin, tiles_m, tiles_n, kLogitsGroupM, tm, tn);
-    m0 = tm * C::BM;
-    n_beg = (int64_t)tn * C::BN;
-    n_end = n_beg + C::BN < a.V ? n_beg + C::BN : a.V;
-  }
-  const int tid = threadIdx.x;
+  const int tiles_m = (a.rows + C::BM - 1) / C::BM;
+  const int tiles_n = (int)((a.V + C::BN - 1) / C::BN);
+  const int lin = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+  int tm, tn;  // M fastest within a group: blocks sharing a W tile are adjacent
+  grouped_tile(lin, tiles_m, tiles_n, kLogitsGroupM, tm, tn);
+  const int m0 = tm * C::BM;
+  const int64_t n0 = (int64_t)tn * C::BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 
   const S* X = static_cast<const S*>(a.X);
   const S* W = static_cast<const S*>(a.W);
 
   // X: gathered rows anywhere in [BT, H] (one 32-bit range over all of X),
   // or, when X is larger than that, the chunk's rows gathered beforehand
-  // into [rows, H]; W: each tile's rows [n0, n0 + BN).
+  // into [rows, H]; W: this tile's rows [n0, n0 + BN).
   const uint32_t row_bytes = (uint32_t)a.H * (uint32_t)sizeof(S);
   const desc_t xr =
       make_rsrc(X, (uint64_t)(a.x_gathered ? (int64_t)a.rows : a.BT) * a.H * sizeof(S));
+  const int64_t nrows_w = a.V - n0 < C::BN ? a.V - n0 : C::BN;
+  const desc_t wr = make_rsrc(W + n0 * a.H, (uint64_t)nrows_w * a.H * sizeof(S));
   OA la;
   OB lb;
   // The block's target columns are read now, so that the two dependent
@@ -711,6 +703,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
     la.init_indexed(
         tid, [&](int r) -> uint32_t { return (uint32_t)a.idx[m0 + r < a.rows ? m0 + r : 0]; },
         [&](int r, uint32_t e) -> uint32_t { return m0 + r < a.rows ? e * row_bytes : kOOB; });
+  lb.init(tid, [&](int r) -> uint32_t { return r < nrows_w ? (uint32_t)r * row_bytes : kOOB; });
   int64_t tgt[TPT];
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
@@ -718,22 +711,6 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
     tgt[i] = a.targets[tix[i]];
   }
 
-#pragma clang loop unroll(disable)
-  for (int64_t n0 = n_beg; n0 < n_end; n0 += C::BN) {
-  // columns [n0, vend) of this tile are computed and stored
-  const int64_t vend = n_end - n0 < C::BN ? n_end : n0 + C::BN;
-  // Addresses are derived afresh in every tile (an opaque LDS offset of zero
-  // and an opaque copy of the thread index): hoisted out of the tile loop,
-  // they would stay live across it and double the registers.
-  uint32_t lds_zero = 0;
-  int tid_t = tid;
-  if constexpr (RANGE) asm volatile("" : "+s"(lds_zero), "+v"(tid_t));
-  unsigned char* smem = smem_raw + lds_zero;
-  const int lane_t = tid_t & 63, wave_t = tid_t >> 6;
-  const int wm_t = wave_t / C::WAVES_N, wn_t = wave_t % C::WAVES_N;
-  const int64_t nrows_w = vend - n0;
-  const desc_t wr = make_rsrc(W + n0 * a.H, (uint64_t)nrows_w * a.H * sizeof(S));
-  lb.init(tid_t, [&](int r) -> uint32_t { return r < nrows_w ? (uint32_t)r * row_bytes : kOOB; });
   f32x16_t acc[C::FM][C::FN];
   zero_acc<C>(acc);
   const int K = (int)a.H;
@@ -741,7 +718,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
   main_loop<T, C, OA, OB, PI::SA, PI::SB, P>(
       [&](unsigned char* tile, int k0, int p) { la.template issue<P>(xr, tile, k0, K, p); },
       [&](unsigned char* tile, int k0, int p) { lb.template issue<P>(wr, tile, k0, K, p); },
-      (K + KT<T, C>::BK - 1) / KT<T, C>::BK, smem, wm_t, wn_t, lane_t, acc);
+      (K + KT<T, C>::BK - 1) / KT<T, C>::BK, smem_raw, wm, wn, lane, acc);
 
   // Epilogue: add the bias (when given; PR #1554, Tests: bias on and off),
   // store the logits relative to their 64-column block maximum (z - max, in
@@ -753,23 +730,22 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
   // The block's target columns go after the staging area (the operand
   // stages are free once the main loop is done; the epilogue's first barrier
   // publishes them).
-  int64_t* tgt_s = reinterpret_cast<int64_t*>(smem + SM::EPI);
+  int64_t* tgt_s = reinterpret_cast<int64_t*>(smem_raw + SM::EPI);
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
-    const int m = tid_t + i * C::NT;
+    const int m = tid + i * C::NT;
     if (m < C::BM) tgt_s[m] = m0 + m < a.rows ? tgt[i] : -1;
   }
   S* slab = static_cast<S*>(a.slab);
   float2* stats = reinterpret_cast<float2*>(a.stats);
   const S* bias = static_cast<const S*>(a.bias);
-  staged_epilogue<C>(reinterpret_cast<float*>(smem), acc, wm_t, wn_t, lane_t, tid_t,
+  staged_epilogue<C>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
                      [&](int brow, int bcol, float (&v)[8]) __attribute__((always_inline)) {
-    // Branch-free except where a piece straddles the end of the tile's
-    // columns: columns past it are masked to -inf for the statistics by
-    // selects.
+    // Branch-free except where a piece straddles the end of the vocabulary:
+    // columns past V are masked to -inf for the statistics by selects.
     const int gm = m0 + brow;
     const int64_t gn = n0 + bcol;
-    const int64_t left = vend - gn;
+    const int64_t left = a.V - gn;
     const int nv = left >= 8 ? 8 : (left > 0 ? (int)left : 0);  // valid columns here
     if (bias) {
       if (nv == 8) {
@@ -834,9 +810,6 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
     for (int e = 0; e < 8; ++e) zt = d == e ? v[e] : zt;
     if (d >= 0 && d < 8) a.ztgt[gm] = zt;
   });
-  if constexpr (!RANGE) break;  // one tile
-  __syncthreads();  // the next tile's loads reuse the staging area
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1104,36 +1077,10 @@ struct DwSmem : Smem<C, DmaCols<T, C, C::BM>, DmaRows<T, C, C::BN>, DwPipe<C>::S
 
 template <class T, class C>
 static hipError_t launch_logits_t(const LogitsArgs& a, hipStream_t st) {
-  static const hipError_t prep = allow_lds(logits_kernel<T, C, false>, LogitsSmem<T, C>::BYTES);
+  static const hipError_t prep = allow_lds(logits_kernel<T, C>, LogitsSmem<T, C>::BYTES);
   if (prep != hipSuccess) return prep;
-  const int tiles_m = (a.rows + C::BM - 1) / C::BM;
-  const int64_t tiles_n = (a.V + C::BN - 1) / C::BN;
-  LogitsArgs b = a;
-  b.cols_per_block = 0;
-  int64_t grid = tiles_m * tiles_n;
-  // One row tile whose column tiles leave the last round of workgroups part
-  // empty (V 151936 in 128-column tiles: 1187 tiles on 512 slots, 2.32 rounds
-  // run as 3): give each workgroup a contiguous range of about V / slots
-  // columns instead, in whole 64-column blocks, when that shortens the
-  // makespan (the tiles a workgroup walks, its columns / BN) by over 5 %.
-  // (The 128 x 128 tile only: walking tiles in a loop costs the large tiles
-  // registers they do not have.)
-  const int64_t slots = 256 * C::WGS;
-  if constexpr (std::is_same<C, Small>::value) if (tiles_m == 1 && tiles_n > slots) {
-    const int64_t cpb = ((a.V + slots - 1) / slots + 63) / 64 * 64;
-    const double rounds = (double)((tiles_n + slots - 1) / slots);
-    if ((double)cpb / C::BN < 0.95 * rounds) {
-      static const hipError_t prep_r =
-          allow_lds(logits_kernel<T, C, true>, LogitsSmem<T, C>::BYTES);
-      if (prep_r != hipSuccess) return prep_r;
-      b.cols_per_block = cpb;
-      grid = (a.V + cpb - 1) / cpb;
-      logits_kernel<T, C, true>
-          <<<dim3((unsigned)grid), dim3(C::NT), LogitsSmem<T, C>::BYTES, st>>>(b);
-      return hipGetLastError();
-    }
-  }
-  logits_kernel<T, C, false><<<dim3((unsigned)grid), dim3(C::NT), LogitsSmem<T, C>::BYTES, st>>>(b);
+  const int tiles = ((a.rows + C::BM - 1) / C::BM) * (int)((a.V + C::BN - 1) / C::BN);
+  logits_kernel<T, C><<<dim3(tiles), dim3(C::NT), LogitsSmem<T, C>::BYTES, st>>>(a);
   return hipGetLastError();
 }
 template <class T, class C>
