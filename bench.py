@@ -710,10 +710,11 @@ def autograd_bench(a, cfg, dev):
 
 PROTOCOL_WORKLOADS = [
     "llama3_8b_lm_head", "llama3_8b_lm_head_c256", "same_dtype_sweep_bf16",
-    "same_dtype_sweep_f16", "same_dtype_sweep_f32", "long_seq_8k_c256", "long_seq_32k_c256",
-    "long_seq_32k_default", "masked_sft_100_trained", "masked_sft_75_trained",
-    "masked_sft_50_trained", "masked_sft_10_trained", "masked_sft_100_frozen",
-    "masked_sft_10_frozen"]
+    "same_dtype_sweep_f16", "same_dtype_sweep_f32", "long_seq_8k_c256", "long_seq_8k_default",
+    "long_seq_32k_c256", "long_seq_32k_default",
+    *[f"masked_sft_{p}_{m}" for m in ("trained", "frozen") for p in (100, 75, 50, 10)],
+    *[f"masked_sft_{p}_{m}_none" for m in ("trained", "frozen") for p in (100, 75, 50, 10)],
+    *[f"masked_sft_packed_{p}_{m}" for m in ("trained", "frozen") for p in (75, 50, 10)]]
 
 
 def protocol(a, dev):
