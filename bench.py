@@ -109,6 +109,13 @@ def parse():
                    help="time the differentiable path instead (forward + loss.backward() "
                         "through fused_linear_cross_entropy, weight-dtype dW) and print "
                         "one {\"autograd\": ...} line")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the probes of what the chip sustains by itself (bf16 MFMA loop "
+                        "with random and with zero operands, HBM read stream, device copy)")
+    p.add_argument("--zero-operands", action="store_true",
+                   help="diagnostic: run the workload with X and W zeroed, so that the MFMA "
+                        "multipliers do not toggle and the power limit does not lower the "
+                        "clock; the line is marked as such and is not a benchmark result")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run plain 1 GiB device copies (reference for HBM byte counters)")
     p.add_argument("--record-traffic", nargs=4, metavar=("KERNEL", "WORKLOAD", "FETCH_CSV",
@@ -389,6 +396,89 @@ def roofline(res, cfg):
     if flops:
         out["mfma_frac"] = flops / sec / 1e12 / peak_f
     return out
+
+
+def ceilings(dev):
+    """What the chip sustains by itself, from the probe library (include/flce_probe.h):
+    bf16 MFMA throughput of a loop with no memory traffic, with random operands (the
+    multipliers toggle as in the GEMMs, and the power limit sets the clock) and with
+    zero operands (no toggling); the HBM read rate of a plain streaming read of 2 GiB;
+    a 1 GiB device copy (read + write).  Each is timed with HIP events on the current
+    stream over several launches after one untimed launch."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "linear_cross_entropy_chunked_amd", "libflce_probe.so"))
+    lib.flce_probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p]
+    lib.flce_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    st = torch.cuda.current_stream(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def timed(launch, reps):
+        launch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            launch()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    def check(rc, what):
+        if rc:
+            raise RuntimeError(f"{what}: status {rc}")
+
+    blocks, iters = 4 * cus, 4000
+    sink = torch.empty(blocks * lib.flce_probe_mfma_threads(), dtype=torch.float32, device=dev)
+    gen = torch.Generator().manual_seed(20240611)
+    rnd = (torch.randn(8 << 20, generator=gen) * 0.05).to(torch.bfloat16).to(dev)
+    flops = blocks * 8 * iters * 32 * 2 * 32 * 32 * 16
+    out = {}
+    for kind, ops in (("random", rnd), ("zero", torch.zeros_like(rnd))):
+        sec = timed(lambda: check(lib.flce_probe_mfma_loop(
+            ops.data_ptr(), ops.numel() * 2, sink.data_ptr(), sink.numel(), blocks, iters,
+            st.cuda_stream), "flce_probe_mfma_loop"), 12)
+        out[f"mfma_loop_bf16_{kind}_tflops"] = flops / sec / 1e12
+    del rnd, sink
+    nbytes = 2 << 30
+    sblocks = nbytes >> 20  # 1 MiB per workgroup
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    ssink = torch.empty(sblocks * lib.flce_probe_stream_threads() * 16, dtype=torch.uint8,
+                        device=dev)
+    sec = timed(lambda: check(lib.flce_probe_read_stream(
+        src.data_ptr(), nbytes, ssink.data_ptr(), ssink.numel(), sblocks, st.cuda_stream),
+        "flce_probe_read_stream"), 10)
+    out["hbm_read_stream_gbs"] = nbytes / sec / 1e9
+    del src, ssink
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    sec = timed(lambda: b.copy_(a), 10)
+    out["hbm_copy_gbs"] = 2 * COPY_BYTES / sec / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    out["how"] = (f"probe library: {blocks} workgroups x 8 waves x {iters} iterations of 32 "
+                  f"independent v_mfma_f32_32x32x16_bf16 on register operands (random: "
+                  f"N(0, 0.05) in bf16; zero: all zero), timed over 12 launches; a read of "
+                  f"2 GiB in {sblocks} contiguous 1 MiB segments, one per workgroup of 256, "
+                  f"16 B per lane, 4 loads in flight per lane, over 10 launches; torch copy "
+                  f"of 1 GiB (2 GiB moved) over 10 launches")
+    return out
+
+
+def add_ceiling(rl, ceil, dtype):
+    """The dominant kernel's rate against what the chip sustains by itself."""
+    if not ceil:
+        return
+    if rl["bound"] == "mfma" and dtype in ("bf16", "f16"):
+        c = ceil["mfma_loop_bf16_random_tflops"]
+        rl["ceiling"] = dict(value=c, unit="TFLOP/s", kind="bf16 MFMA loop, random operands")
+        rl["frac_of_ceiling"] = rl["achieved"] / c
+    elif rl["bound"] == "hbm":
+        c = ceil["hbm_read_stream_gbs"]
+        rl["ceiling"] = dict(value=c, unit="GB/s", kind="HBM read stream")
+        rl["frac_of_ceiling"] = rl["achieved"] / c
 
 
 def cpu_baseline(host, cfg, rows):
@@ -878,11 +968,17 @@ def main():
         autograd_bench(a, cfg, dev)
         return
     t_start = time.perf_counter()
-    main_res, host = run_workload(a.workload, cfg, a.steps, a.warmup, dev,
+    host_dev = None
+    if a.zero_operands:
+        host, (X, W, t) = make_inputs(cfg, dev)
+        host_dev = (host, (torch.zeros_like(X), torch.zeros_like(W), t))
+        del X, W
+    main_res, host = run_workload(a.workload, cfg, a.steps, a.warmup, dev, host_dev=host_dev,
                                   sensor_s=a.sensor_seconds)
+    del host_dev
     main_res["kernel_rates"] = kernel_rates(main_res, cfg)
     cpu = None
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and not a.zero_operands:
         cpu = cpu_baseline(host, cfg, a.cpu_rows)
     del host
     extras = {}
@@ -897,6 +993,12 @@ def main():
         extras[name] = res
         torch.cuda.empty_cache()
     summaries = extra_summaries(extras)
+    ceil = None
+    if not a.no_ceilings:
+        log("ceilings: MFMA loop (random, zero operands), HBM read stream, device copy")
+        ceil = ceilings(dev)
+        for name, res in extras.items():
+            add_ceiling(res["roofline"], ceil, WORKLOADS[name]["dtype"])
     rl = roofline(main_res, cfg)
     rl["traffic"] = recorded_traffic(rl["kernel"], a.workload)
     sens = main_res["gpu_sensors"]
@@ -907,6 +1009,7 @@ def main():
         if mhz:
             rl["frac_at_measured_clock"] = rl["frac"] * 2400.0 / mhz
             rl["measured_clock_mhz"] = mhz
+    add_ceiling(rl, ceil, cfg["dtype"])
     out = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],
@@ -919,17 +1022,21 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg["dtype"],
-        "data": "synthetic",
+        "data": "synthetic" + (", X and W zeroed (diagnostic, not a benchmark result)"
+                                if a.zero_operands else ""),
         "config": {"workload": a.workload, "BT": cfg["BT"], "H": cfg["H"], "V": cfg["V"],
                    "chunk_size": main_res["chunk_size"], "accum_dtype": cfg["accum"],
                    "reduction": cfg["reduction"], "labelled_share": cfg["share"],
-                   "seq_len": main_res["seq_len"], "frozen_weight": main_res["frozen_weight"]},
+                   "seq_len": main_res["seq_len"], "frozen_weight": main_res["frozen_weight"],
+                   **({"operands": "zero"} if a.zero_operands else {})},
         "mfma_frac_of_peak": main_res["mfma_frac"],
         "algorithmic_tflops": main_res["algorithmic_tflops"],
         "roofline": rl,
     }
     if cpu is not None:
         out["cpu_baseline"] = cpu
+    if ceil is not None:
+        out["ceilings"] = ceil
     out["detail"] = main_res
     out["summaries"] = summaries
     out["extra"] = extras

@@ -1,8 +1,10 @@
-"""Build the gfx950 HIP library ``libflce.so`` in-tree with hipcc.
+"""Build the gfx950 HIP libraries in-tree with hipcc.
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instructions
-disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``), then linked
-into one shared library next to this file.
+disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``).  The path's
+sources are linked into ``libflce.so`` (the C ABI of ``include/flce.h``); the
+benchmark's measurement probes (``include/flce_probe.h``) into a library of
+their own, ``libflce_probe.so``, both next to this file.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libflce.so")
 SOURCES = ["flce_api.hip", "flce_gemm.hip", "flce_rowops.hip"]
+PROBE_LIB = os.path.join(PKG, "libflce_probe.so")
+PROBE_SOURCES = ["flce_probe.hip"]
 
 
 def hipcc() -> str:
@@ -51,11 +55,14 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             print("\n".join(errs), file=sys.stderr)
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    subprocess.run([cc, "--offload-arch=gfx950", "-shared", "-o", tmp, *objs], check=True)
-    os.replace(tmp, LIB)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(compile_one, srcs)))
+    for lib, group in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        tmp = lib + ".tmp"
+        subprocess.run([cc, "--offload-arch=gfx950", "-shared", "-o", tmp,
+                        *(objs[s] for s in group)], check=True)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -1,6 +1,7 @@
 """Host-side checks of the C-ABI library (no GPU needed, no compute launched).
 
-* the library loads and exports every function include/flce.h declares;
+* the library loads and exports every function include/flce.h declares, and
+  the benchmark's probe library every function include/flce_probe.h declares;
 * the chunk policy reproduces every geometry the pages print;
 * workspace sizing follows the slab formula and is flat in BT for an
   explicit chunk size;
@@ -16,8 +17,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 
-def _header_functions():
-    src = open(os.path.join(ROOT, "include", "flce.h")).read()
+def _header_functions(header="flce.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(flce_[a-z0-9_]+)\s*\(", src)))
 
@@ -37,6 +38,34 @@ def test_exported_symbols_in_dynamic_table(flce_lib):
     syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
     for name in _header_functions():
         assert name in syms
+
+
+def test_probe_library_exports_its_header(flce_lib):
+    import ctypes
+    import subprocess
+    path = os.path.join(os.path.dirname(flce_lib.LIB_PATH), "libflce_probe.so")
+    declared = _header_functions("flce_probe.h")
+    assert declared == ["flce_probe_mfma_loop", "flce_probe_mfma_threads",
+                        "flce_probe_read_stream", "flce_probe_stream_threads"]
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    assert set(declared) <= syms
+    lib = ctypes.CDLL(path)
+    assert lib.flce_probe_mfma_threads() == 512
+    assert lib.flce_probe_stream_threads() == 256
+    # invalid arguments are refused before any launch
+    lib.flce_probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p]
+    lib.flce_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    far = 1 << 44
+    assert lib.flce_probe_mfma_loop(far, 16, far, 511, 1, 1, None) == 1   # sink too small
+    assert lib.flce_probe_mfma_loop(far, 8, far, 512, 1, 1, None) == 1    # no whole fragment
+    assert lib.flce_probe_mfma_loop(None, 16, far, 512, 1, 1, None) == 1
+    assert lib.flce_probe_read_stream(far, 24, far, 4096, 1, None) == 1   # not a multiple of 16
+    assert lib.flce_probe_read_stream(far, 32, far, 4095, 1, None) == 1   # sink too small
 
 
 def test_status_and_kernel_names(flce_lib):

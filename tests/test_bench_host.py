@@ -70,3 +70,20 @@ def test_extra_summaries():
     assert abs(rows[1]["speedup"] - 2.0) < 1e-12 and rows[2]["chunk_ratio"] == 64 / 7
     f = s["flat_transient_c256"]
     assert f["workspace_difference_bytes"] == f["row_index_and_loss_bytes"] == 8 * 24576
+
+
+def test_ceiling_fraction_follows_the_bound():
+    ceil = {"mfma_loop_bf16_random_tflops": 1600.0, "mfma_loop_bf16_zero_tflops": 2400.0,
+            "hbm_read_stream_gbs": 6000.0, "hbm_copy_gbs": 5000.0}
+    rl = dict(bound="mfma", achieved=800.0)
+    bench.add_ceiling(rl, ceil, "bf16")
+    assert rl["frac_of_ceiling"] == 0.5 and rl["ceiling"]["unit"] == "TFLOP/s"
+    rl = dict(bound="hbm", achieved=4500.0)
+    bench.add_ceiling(rl, ceil, "bf16")
+    assert rl["frac_of_ceiling"] == 0.75 and rl["ceiling"]["unit"] == "GB/s"
+    # an fp32 contraction has no bf16 loop to compare with; no probes, no fields
+    rl = dict(bound="mfma", achieved=100.0)
+    bench.add_ceiling(rl, ceil, "f32")
+    assert "frac_of_ceiling" not in rl
+    bench.add_ceiling(rl, None, "bf16")
+    assert "frac_of_ceiling" not in rl
