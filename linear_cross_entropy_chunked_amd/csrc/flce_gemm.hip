@@ -63,6 +63,13 @@ template <class C> struct LogitsPipe { static constexpr int SA = 2, SB = 3, P = 
 template <> struct LogitsPipe<Big8M> { static constexpr int SA = 2, SB = 3, P = 1; };
 template <class C> struct DxPipe { static constexpr int SA = 3, SB = 2, P = 2; };
 template <> struct DxPipe<Big8N> { static constexpr int SA = 2, SB = 3, P = 1; };
+// grad_input with the eight-wave tile when a chunk fills it (more than 128
+// rows): three stages of G, two of W.  Measured interleaved against
+// DxPipe<Big8N>: Llama shape chunk 2048 1.75 -> 1.68 ms per launch, chunk 256
+// 247 -> 238 us, H 5376 / V 262144 chunk 256 644 -> 627 us; with 128-row
+// chunks, where half the G tile is empty and W streams from HBM, W's third
+// stage wins (138 against 150 us).
+struct DxPipeG3 { static constexpr int SA = 3, SB = 2, P = 1; };
 template <class C> struct DwPipe { static constexpr int SA = 2, SB = 3, P = 4; };
 template <> struct DwPipe<Big8M> { static constexpr int SA = 3, SB = 2, P = 1; };
 
@@ -831,12 +838,11 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
 // grad_input: dX[idx[m], n] = s * sum_k G[m, k] W[k, n] over one split of k,
 // or, with splits > 1, fp32 partials part[split][m][n] reduced afterwards.
 // ---------------------------------------------------------------------------
-template <class T, class C>
+template <class T, class C, class PI>
 __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void dx_kernel(DxArgs a) {
   typedef typename T::storage S;
   typedef DmaRows<T, C, C::BM> OA;
   typedef DmaCols<T, C, C::BN> OB;
-  typedef DxPipe<C> PI;
   extern __shared__ __align__(16) unsigned char smem_raw[];
 
   const int tiles_m = (a.rows + C::BM - 1) / C::BM;
@@ -1083,9 +1089,8 @@ static hipError_t allow_lds(K kernel, size_t bytes) {
 template <class T, class C>
 struct LogitsSmem : Smem<C, DmaRows<T, C, C::BM>, DmaRows<T, C, C::BN>, LogitsPipe<C>::SA,
                          LogitsPipe<C>::SB, C::BM * sizeof(int64_t)> {};
-template <class T, class C>
-struct DxSmem : Smem<C, DmaRows<T, C, C::BM>, DmaCols<T, C, C::BN>, DxPipe<C>::SA,
-                     DxPipe<C>::SB> {};
+template <class T, class C, class PI>
+struct DxSmem : Smem<C, DmaRows<T, C, C::BM>, DmaCols<T, C, C::BN>, PI::SA, PI::SB> {};
 template <class T, class C>
 struct DwSmem : Smem<C, DmaCols<T, C, C::BM>, DmaRows<T, C, C::BN>, DwPipe<C>::SA,
                      DwPipe<C>::SB> {};
@@ -1098,12 +1103,12 @@ static hipError_t launch_logits_t(const LogitsArgs& a, hipStream_t st) {
   logits_kernel<T, C><<<dim3(tiles), dim3(C::NT), LogitsSmem<T, C>::BYTES, st>>>(a);
   return hipGetLastError();
 }
-template <class T, class C>
+template <class T, class C, class PI = DxPipe<C>>
 static hipError_t launch_dx_t(const DxArgs& a, hipStream_t st) {
-  static const hipError_t prep = allow_lds(dx_kernel<T, C>, DxSmem<T, C>::BYTES);
+  static const hipError_t prep = allow_lds(dx_kernel<T, C, PI>, DxSmem<T, C, PI>::BYTES);
   if (prep != hipSuccess) return prep;
   const int tiles = ((a.rows + C::BM - 1) / C::BM) * (int)((a.H + C::BN - 1) / C::BN) * a.splits;
-  dx_kernel<T, C><<<dim3(tiles), dim3(C::NT), DxSmem<T, C>::BYTES, st>>>(a);
+  dx_kernel<T, C, PI><<<dim3(tiles), dim3(C::NT), DxSmem<T, C, PI>::BYTES, st>>>(a);
   return hipGetLastError();
 }
 template <class T, class C, class D>
@@ -1152,8 +1157,10 @@ template <class T>
 static hipError_t dx_t(const DxArgs& a, hipStream_t st) {
   constexpr bool k16 = sizeof(typename T::storage) == 2;
   typedef typename std::conditional<k16, Big8N, Big>::type L;
-  return dx_shape(a.rows, a.H, k16) == Shape::Big ? launch_dx_t<T, L>(a, st)
-                                                  : launch_dx_t<T, Small>(a, st);
+  if (dx_shape(a.rows, a.H, k16) != Shape::Big) return launch_dx_t<T, Small>(a, st);
+  if constexpr (k16)
+    if (a.rows > 128) return launch_dx_t<T, L, DxPipeG3>(a, st);
+  return launch_dx_t<T, L>(a, st);
 }
 template <class T, class D>
 static hipError_t dw_t(const DwArgs& a, hipStream_t st) {
