@@ -1129,8 +1129,9 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t st) {
 // in one part), grad_input 1.92 -> 1.73 ms (128 x 64 wave tiles), grad_weight
 // 2.60 -> 2.32 ms (64 x 128, three stages of G).  256 x 128 tiles with two
 // workgroups per CU reached 2.40 ms for grad_weight but were 15-25 % slower
-// for logits and grad_input, whose k loops they leave bound by LDS traffic
-// (half the operand reuse per workgroup).  fp32 keeps the four-wave tile.
+// for logits and grad_input, whose k loops then load twice the operand bytes
+// per MFMA (half the operand reuse per workgroup).  fp32 keeps the four-wave
+// tile.
 // For 16-bit operands grad_input and grad_weight take the eight-wave tile at
 // any chunk size ("wide"): with few rows per chunk, where the dW
 // read-modify-write bounds grad_weight, a 256 x 256 tile moves four times the
