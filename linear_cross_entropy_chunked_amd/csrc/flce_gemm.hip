@@ -53,6 +53,7 @@ typedef Cfg<256, 256, 128, 1> Big;         // 4 waves of 128 x 128 (fp32 operand
 typedef Cfg<256, 256, 128, 1, 4, 2> Big8M;  // 8 waves of 64 x 128 (16-bit logits, grad_weight)
 typedef Cfg<256, 256, 128, 1, 2, 4> Big8N;  // 8 waves of 128 x 64 (16-bit grad_input)
 typedef Cfg<128, 128, 128, 2> Small;        // 4 waves of 64 x 64, 2 workgroups per CU
+typedef Cfg<128, 128, 256, 1, 2, 4> SmallK; // 8 waves of 64 x 32, 256-byte k rows (16-bit logits, <= 128 rows)
 
 // LDS stages per operand (SA, SB) and the parts P each k-tile's loads are
 // split into, per kernel and tile shape (measured on MI355X).  A tile is
@@ -61,6 +62,7 @@ typedef Cfg<128, 128, 128, 2> Small;        // 4 waves of 64 x 64, 2 workgroups 
 // tile's loads over the k-steps of the previous tile's MFMA work.
 template <class C> struct LogitsPipe { static constexpr int SA = 2, SB = 3, P = 2; };
 template <> struct LogitsPipe<Big8M> { static constexpr int SA = 2, SB = 3, P = 1; };
+template <> struct LogitsPipe<SmallK> { static constexpr int SA = 2, SB = 3, P = 1; };
 template <class C> struct DxPipe { static constexpr int SA = 3, SB = 2, P = 2; };
 template <> struct DxPipe<Big8N> { static constexpr int SA = 2, SB = 3, P = 1; };
 // grad_input with the eight-wave tile when a chunk fills it (more than 128
@@ -156,12 +158,15 @@ template <class T, int RB_>
 struct RowSwz {
   typedef typename T::storage S;
   static constexpr int RB = RB_;
-  static_assert(RB == 64 || RB == 128, "row swizzle assumes 64- or 128-byte rows");
+  static_assert(RB == 64 || RB == 128 || RB == 256, "row swizzle assumes 64-, 128- or 256-byte rows");
   static constexpr size_t bytes(int R) { return (size_t)R * RB; }
   // LDS serves 256 bytes per cycle (64 banks): the 16 rows read by 16
   // consecutive lanes must land in 16 distinct 16-byte slots of that window.
-  // 128-byte rows: chunk ^= (r / 2) % 8; 64-byte rows: chunk ^= (r / 4) % 4.
-  __device__ __forceinline__ static int swz(int r) { return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+  // 256-byte rows: chunk ^= r % 16; 128-byte rows: chunk ^= (r / 2) % 8;
+  // 64-byte rows: chunk ^= (r / 4) % 4.
+  __device__ __forceinline__ static int swz(int r) {
+    return RB == 256 ? (r & 15) : RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+  }
   __device__ __forceinline__ static u32x4_t frag16(const unsigned char* b, int r, int s, int lane) {
     const int kc = 2 * s + (lane >> 5);
     return *reinterpret_cast<const u32x4_t*>(b + r * RB + ((kc ^ swz(r)) << 4));
@@ -1137,8 +1142,12 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t st) {
 // read-modify-write bounds grad_weight, a 256 x 256 tile moves four times the
 // bytes per load round trip of a 128 x 128 one (grad_weight at chunk 256:
 // 0.95 -> 0.89 ms with fp32 dW, 2.24 -> 1.72 ms with bf16 dW at H 5376,
-// V 262144; at chunk 128 both GEMMs 9-12 % faster).  Logits keep the
-// 128 x 128 tile for chunks of at most 128 rows (7-11 % faster there).
+// V 262144; at chunk 128 both GEMMs 9-12 % faster).  Logits keep a
+// 128 x 128 tile for chunks of at most 128 rows (7-11 % faster there than
+// 256 x 256); with 16-bit operands it is eight waves over k-tiles of 256
+// bytes per row (one workgroup per CU), whose longer runs per W row the
+// memory streams faster at H 2048 (masked SFT chunk 128: 174.6 -> 170.9 us
+// trained, 166.6 -> 161.7 us frozen per launch).
 enum class Shape { Small, Big };
 Shape logits_shape(int rows, int64_t V) { return rows > 128 && V >= 1024 ? Shape::Big : Shape::Small; }
 Shape dx_shape(int rows, int64_t H, bool wide) {
@@ -1150,9 +1159,11 @@ Shape dw_shape(int rows, int64_t H, bool wide) {
 
 template <class T>
 static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
-  typedef typename std::conditional<sizeof(typename T::storage) == 2, Big8M, Big>::type L;
+  constexpr bool k16 = sizeof(typename T::storage) == 2;
+  typedef typename std::conditional<k16, Big8M, Big>::type L;
+  typedef typename std::conditional<k16, SmallK, Small>::type LS;
   return logits_shape(a.rows, a.V) == Shape::Big ? launch_logits_t<T, L>(a, st)
-                                                 : launch_logits_t<T, Small>(a, st);
+                                                 : launch_logits_t<T, LS>(a, st);
 }
 template <class T>
 static hipError_t dx_t(const DxArgs& a, hipStream_t st) {
@@ -1196,7 +1207,8 @@ DxTile dx_tile(int dtype, int rows, int64_t H) {
 }
 // Column width of one (max, sum exp) entry written by the logits GEMM.
 int stats_cols() {
-  static_assert(Big::FN % 2 == 0 && Big8M::FN % 2 == 0 && Small::FN % 2 == 0,
+  static_assert(Big::BN % 64 == 0 && Big8M::BN % 64 == 0 && Small::BN % 64 == 0 &&
+                    SmallK::BN % 64 == 0,
                 "64-column stats blocks");
   return 64;
 }

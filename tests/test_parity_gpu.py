@@ -148,19 +148,22 @@ def test_repeated_calls_are_bit_identical(pkg, dtype, shape):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("chunk", [64, 128])
-def test_streaming_logits_path(pkg, dtype, chunk):
-    """Chunks of at most 128 rows with a vocabulary of 16384 or more take the
-    logits tile that keeps seven W tiles in flight (one workgroup per CU);
-    ragged V and several chunks, a ragged last one included."""
-    BT, H, V = 330, 72, 20001
-    X, W, t = si.make_case(BT, H, V, dtype, 4100 + chunk, ignore="scattered", frac=0.15)
+@pytest.mark.parametrize("H", [72, 328])
+def test_small_chunk_logits_path(pkg, dtype, chunk, H):
+    """Chunks of at most 128 rows take the 128 x 128 logits tile: for 16-bit
+    operands eight waves over k-tiles of 128 elements (H 72: one partial
+    k-tile; H 328: two whole ones and a partial one), for fp32 four waves over
+    32-element k-tiles.  Ragged V and several chunks, a ragged last one
+    included."""
+    BT, V = 330, 20001
+    X, W, t = si.make_case(BT, H, V, dtype, 4100 + chunk + H, ignore="scattered", frac=0.15)
     r = _run(pkg, X, W, t, reduction="mean", chunk_size=chunk, accum_dtype=torch.float32)
     ref = oracle.flce(X, W, t, reduction="mean")
     assert r.stats["chunk_size"] == chunk and r.stats["n_valid"] == ref["n_valid"]
     _check(r, ref, dtype, "mean")
 
 
-def test_streaming_logits_path_with_options(pkg):
+def test_small_chunk_logits_path_with_options(pkg):
     """The same tile with a bias, the z-loss and the predicted token."""
     BT, H, V = 200, 64, 17000
     X, W, t = si.make_case(BT, H, V, "bf16", 4200, ignore="scattered", frac=0.2)
