@@ -54,6 +54,7 @@ typedef Cfg<256, 256, 128, 1, 4, 2> Big8M;  // 8 waves of 64 x 128 (16-bit logit
 typedef Cfg<256, 256, 128, 1, 2, 4> Big8N;  // 8 waves of 128 x 64 (16-bit grad_input)
 typedef Cfg<128, 128, 128, 2> Small;        // 4 waves of 64 x 64, 2 workgroups per CU
 typedef Cfg<128, 128, 256, 1, 2, 4> SmallK; // 8 waves of 64 x 32, 256-byte k rows (16-bit logits, <= 128 rows)
+typedef Cfg<128, 256, 128, 1, 2, 4> Mid8N;  // 8 waves of 64 x 64 (16-bit grad_input, <= 128 rows)
 
 // LDS stages per operand (SA, SB) and the parts P each k-tile's loads are
 // split into, per kernel and tile shape (measured on MI355X).  A tile is
@@ -64,14 +65,14 @@ template <class C> struct LogitsPipe { static constexpr int SA = 2, SB = 3, P = 
 template <> struct LogitsPipe<Big8M> { static constexpr int SA = 2, SB = 3, P = 1; };
 template <> struct LogitsPipe<SmallK> { static constexpr int SA = 2, SB = 3, P = 1; };
 template <class C> struct DxPipe { static constexpr int SA = 3, SB = 2, P = 2; };
-template <> struct DxPipe<Big8N> { static constexpr int SA = 2, SB = 3, P = 1; };
-// grad_input with the eight-wave tile when a chunk fills it (more than 128
-// rows): three stages of G, two of W.  Measured interleaved against
-// DxPipe<Big8N>: Llama shape chunk 2048 1.75 -> 1.68 ms per launch, chunk 256
-// 247 -> 238 us, H 5376 / V 262144 chunk 256 644 -> 627 us; with 128-row
-// chunks, where half the G tile is empty and W streams from HBM, W's third
-// stage wins (138 against 150 us).
+// grad_input with the eight-wave tile (chunks of more than 128 rows): three
+// stages of G, two of W.  Measured interleaved against two of G and three of
+// W: Llama shape chunk 2048 1.75 -> 1.68 ms per launch, chunk 256 247 -> 238
+// us, H 5376 / V 262144 chunk 256 644 -> 627 us.
 struct DxPipeG3 { static constexpr int SA = 3, SB = 2, P = 1; };
+// grad_input of chunks of at most 128 rows: a 128-row tile, whose G stages
+// are half the size, leaves room for four stages of the W stream.
+template <> struct DxPipe<Mid8N> { static constexpr int SA = 2, SB = 4, P = 1; };
 template <class C> struct DwPipe { static constexpr int SA = 2, SB = 3, P = 4; };
 template <> struct DwPipe<Big8M> { static constexpr int SA = 3, SB = 2, P = 1; };
 
@@ -1171,8 +1172,9 @@ static hipError_t dx_t(const DxArgs& a, hipStream_t st) {
   typedef typename std::conditional<k16, Big8N, Big>::type L;
   if (dx_shape(a.rows, a.H, k16) != Shape::Big) return launch_dx_t<T, Small>(a, st);
   if constexpr (k16)
-    if (a.rows > 128) return launch_dx_t<T, L, DxPipeG3>(a, st);
-  return launch_dx_t<T, L>(a, st);
+    return a.rows > 128 ? launch_dx_t<T, L, DxPipeG3>(a, st) : launch_dx_t<T, Mid8N>(a, st);
+  else
+    return launch_dx_t<T, L>(a, st);
 }
 template <class T, class D>
 static hipError_t dw_t(const DwArgs& a, hipStream_t st) {
@@ -1202,8 +1204,9 @@ hipError_t launch_dw(int dtype, const DwArgs& a, hipStream_t st) {
 DxTile dx_tile(int dtype, int rows, int64_t H) {
   static_assert(Big::BM == Big8N::BM && Big::BN == Big8N::BN && Big::WGS == Big8N::WGS,
                 "both large grad_input tiles split k alike");
-  return dx_shape(rows, H, dtype != 0) == Shape::Big ? DxTile{Big::BM, Big::BN, Big::WGS}
-                                                     : DxTile{Small::BM, Small::BN, Small::WGS};
+  if (dx_shape(rows, H, dtype != 0) != Shape::Big) return DxTile{Small::BM, Small::BN, Small::WGS};
+  if (dtype != 0 && rows <= 128) return DxTile{Mid8N::BM, Mid8N::BN, Mid8N::WGS};
+  return DxTile{Big::BM, Big::BN, Big::WGS};
 }
 // Column width of one (max, sum exp) entry written by the logits GEMM.
 int stats_cols() {
