@@ -214,57 +214,75 @@ hipError_t launch_zero_ignored(const int64_t* targets, int64_t BT, int64_t H,
 // ---------------------------------------------------------------------------
 constexpr int SM_T = 256;
 
+// (max, sum exp rescaled to max, first index of max) of two parts: the sums
+// are rescaled to the larger maximum; of equal maxima the lower index wins.
+// A part with no entries has (-inf, 0, INT_MAX) and leaves the other as is.
+__device__ __forceinline__ void merge_max_sum_first(float& m, float& s, int& f, float m2, float s2,
+                                                    int f2) {
+  const float M = fmaxf(m, m2);
+  const float a = m == M ? s : s * __expf(m - M);
+  const float b = m2 == M ? s2 : s2 * __expf(m2 - M);
+  const int fa = m == M ? f : 0x7fffffff, fb = m2 == M ? f2 : 0x7fffffff;
+  s = a + b;
+  f = fa < fb ? fa : fb;
+  m = M;
+}
+// The same over the 64 lanes of a wave (butterfly: every lane ends with the
+// wave's triple).
+__device__ __forceinline__ void combine_max_sum_first(float& m, float& s, int& f) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(s, o, kWave);
+    const int f2 = __shfl_xor(f, o, kWave);
+    merge_max_sum_first(m, s, f, m2, s2, f2);
+  }
+}
+
 template <class T>
 __global__ __launch_bounds__(SM_T) void softmax_kernel(SoftmaxArgs a) {
   typedef typename T::storage S;
-  __shared__ float red[SM_T / kWave];
+  __shared__ float red[SM_T / kWave], red2[SM_T / kWave];
   __shared__ int ired[SM_T / kWave];
-  __shared__ float bcast;
+  __shared__ float bcast, bcast2;
   __shared__ int ibcast;
   const int m = blockIdx.x / a.parts;
   const int part = blockIdx.x % a.parts;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   const float2* st = reinterpret_cast<const float2*>(a.stats) + (int64_t)m * a.stats_ld;
-  float mx = -INFINITY;
-  for (int64_t j = tid; j < a.stats_n; j += SM_T) mx = fmaxf(mx, st[j].x);
-  mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  if (tid == 0) {
-    float v = red[0];
-    for (int w = 1; w < SM_T / kWave; ++w) v = fmaxf(v, red[w]);
-    bcast = v;
-  }
-  __syncthreads();
-  const float M = bcast;
-  float s = 0.f;
+  // One pass over the row's (block max, block sum exp) pairs: each thread
+  // keeps a running maximum, the sum rescaled to it, and the first block
+  // holding it; the threads' triples are then combined in a fixed tree.
+  float mx = -INFINITY, s = 0.f;
   int first = 0x7fffffff;  // lowest block holding the row maximum
   for (int64_t j = tid; j < a.stats_n; j += SM_T) {
     const float2 p = st[j];
-    s += p.y * __expf(p.x - M);
-    if (p.x == M && (int)j < first) first = (int)j;
+    if (p.x > mx) {
+      s = s * __expf(mx - p.x) + p.y;
+      mx = p.x;
+      first = (int)j;
+    } else {
+      s += p.y * __expf(p.x - mx);
+    }
   }
-  s = wave_sum(s);
-  if (a.amax) first = wave_min_int(first);
-  __syncthreads();
+  combine_max_sum_first(mx, s, first);
   if (lane == 0) {
-    red[wave] = s;
+    red[wave] = mx;
+    red2[wave] = s;
     ired[wave] = first;
   }
   __syncthreads();
   if (tid == 0) {
-    float v = red[0];
+    float v = red[0], t = red2[0];
     int f = ired[0];
-    for (int w = 1; w < SM_T / kWave; ++w) {
-      v += red[w];
-      f = ired[w] < f ? ired[w] : f;
-    }
+    for (int w = 1; w < SM_T / kWave; ++w) merge_max_sum_first(v, t, f, red[w], red2[w], ired[w]);
     bcast = v;
+    bcast2 = t;
     ibcast = f;
   }
   __syncthreads();
-  const float lse = M + logf(bcast);
+  const float M = bcast;
+  const float lse = M + logf(bcast2);
 
   const int64_t row = a.idx[m];
   const int64_t tgt = a.targets[row];
