@@ -703,7 +703,8 @@ def record_traffic(kernel, workload, fetch_csv, write_csv):
         fh.write("# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of:\n")
         fh.write(f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- "
                  f"python bench.py --workload {workload} --steps 1 --warmup 1 "
-                 f"--no-cpu-baseline --extra '' --copy-calibration\n")
+                 f"--no-cpu-baseline --extra '' --sensor-seconds 0 --no-ceilings "
+                 f"--copy-calibration\n")
         fh.write("#   (the same with --pmc WRITE_SIZE -o write)\n")
         fh.write("# counters are KiB per dispatch; each is scaled by the ratio of the bytes a\n")
         fh.write("# 1 GiB device copy moves to what the counter reports for it\n")
