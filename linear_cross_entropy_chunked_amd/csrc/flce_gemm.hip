@@ -18,9 +18,11 @@
 //
 // Tile shapes: 256x256 blocks (one workgroup per CU) of four 128x128 waves
 // for fp32 operands and of eight 64x128 or 128x64 waves (two per SIMD) for
-// 16-bit operands; 128x128 blocks of four 64x64 waves (two workgroups per
-// CU) where the problem is small or, for grad_weight with few rows per
-// chunk, bound by the read-modify-write of dW.
+// 16-bit operands; for chunks of at most 128 rows with 16-bit operands,
+// 128x128 logits blocks of eight 64x32 waves over 256-byte k rows and
+// 128x256 grad_input blocks of eight 64x64 waves; 128x128 blocks of four
+// 64x64 waves (two workgroups per CU) for the other small problems (fp32
+// with few rows, or fewer than 256 hidden units).
 #include <type_traits>
 
 #include "flce_device.hpp"
