@@ -20,7 +20,8 @@
 // for fp32 operands and of eight 64x128 or 128x64 waves (two per SIMD) for
 // 16-bit operands; for chunks of at most 128 rows with 16-bit operands,
 // 128x128 logits blocks of eight 64x32 waves over 256-byte k rows and
-// 128x256 grad_input blocks of eight 64x64 waves; 128x128 blocks of four
+// 128x256 grad_input blocks of eight 64x64 waves and 256x128 grad_weight
+// blocks of eight 64x64 waves, two workgroups per CU; 128x128 blocks of four
 // 64x64 waves (two workgroups per CU) for the other small problems (fp32
 // with few rows, or fewer than 256 hidden units).
 #include <type_traits>
@@ -57,6 +58,7 @@ typedef Cfg<256, 256, 128, 1, 2, 4> Big8N;  // 8 waves of 128 x 64 (16-bit grad_
 typedef Cfg<128, 128, 128, 2> Small;        // 4 waves of 64 x 64, 2 workgroups per CU
 typedef Cfg<128, 128, 256, 1, 2, 4> SmallK; // 8 waves of 64 x 32, 256-byte k rows (16-bit logits, <= 128 rows)
 typedef Cfg<128, 256, 128, 1, 2, 4> Mid8N;  // 8 waves of 64 x 64 (16-bit grad_input, <= 128 rows)
+typedef Cfg<256, 128, 64, 2, 4, 2> Twin8M;  // 8 waves of 64 x 64, 2 workgroups per CU (16-bit grad_weight, <= 128 rows)
 
 // LDS stages per operand (SA, SB) and the parts P each k-tile's loads are
 // split into, per kernel and tile shape (measured on MI355X).  A tile is
@@ -77,6 +79,14 @@ struct DxPipeG3 { static constexpr int SA = 3, SB = 2, P = 1; };
 template <> struct DxPipe<Mid8N> { static constexpr int SA = 2, SB = 4, P = 1; };
 template <class C> struct DwPipe { static constexpr int SA = 2, SB = 3, P = 4; };
 template <> struct DwPipe<Big8M> { static constexpr int SA = 3, SB = 2, P = 1; };
+// grad_weight of chunks of at most 128 rows (16-bit operands): the k loop is
+// a few k-tiles and the dW read-modify-write is the kernel; two workgroups
+// per CU, each 72 KB of LDS (64-byte k rows, three stages of each operand),
+// so that one's read-modify-write overlaps the other's loads and MFMAs.
+// Masked SFT at chunk 128 (bf16 dW): 257 -> 242 us per launch, step 38.9 ->
+// 38.0 ms; at chunk 256 no gain (fp32 dW) or a loss (bf16 dW, 1430 -> 1463 us),
+// at chunk 2048 14 % slower.
+template <> struct DwPipe<Twin8M> { static constexpr int SA = 3, SB = 3, P = 1; };
 
 template <class T, class C>
 struct KT {
@@ -1182,8 +1192,10 @@ template <class T, class D>
 static hipError_t dw_t(const DwArgs& a, hipStream_t st) {
   constexpr bool k16 = sizeof(typename T::storage) == 2;
   typedef typename std::conditional<k16, Big8M, Big>::type L;
-  return dw_shape(a.rows, a.H, k16) == Shape::Big ? launch_dw_t<T, L, D>(a, st)
-                                                  : launch_dw_t<T, Small, D>(a, st);
+  if (dw_shape(a.rows, a.H, k16) != Shape::Big) return launch_dw_t<T, Small, D>(a, st);
+  if constexpr (k16)
+    if (a.rows <= 128) return launch_dw_t<T, Twin8M, D>(a, st);
+  return launch_dw_t<T, L, D>(a, st);
 }
 
 hipError_t launch_logits(int dtype, const LogitsArgs& a, hipStream_t st) {
