@@ -92,28 +92,49 @@ __global__ __launch_bounds__(256) void gather_t_kernel(const S* __restrict__ X,
                                                        const int32_t* __restrict__ idx, int rows,
                                                        int64_t H, S* __restrict__ XcT,
                                                        int64_t ldx) {
-  __shared__ S tile[64][65];
+  // 16-byte vectors both ways: VE elements of one row along h on the way in,
+  // VE rows of one h on the way out.  H is a multiple of 8, so a vector along
+  // h lies wholly inside or outside [0, H).
+  constexpr int VE = 16 / (int)sizeof(S);
+  constexpr int VPR = 64 / VE;             // vectors per 64-element tile row
+  constexpr int PER = 64 * VPR / 256;      // vectors per thread each way
+  __shared__ S tile[64][64 + 2];           // [row][h]; the pad spreads a column over banks
   __shared__ int32_t ridx[64];
   const int r0 = blockIdx.x * 64;
   const int64_t h0 = (int64_t)blockIdx.y * 64;
   const int tid = threadIdx.x;
   if (tid < 64) ridx[tid] = (r0 + tid < rows) ? idx[r0 + tid] : -1;
   __syncthreads();
+  u32x4_t in[PER];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < PER; ++e) {
     const int q = tid + e * 256;
-    const int r = q >> 6, h = q & 63;
+    const int r = q / VPR, hv = (q % VPR) * VE;
     const int32_t src = ridx[r];
-    S v = S(0);
-    if (src >= 0 && h0 + h < H) v = X[(int64_t)src * H + h0 + h];
-    tile[r][h] = v;
+    in[e] = u32x4_t{0u, 0u, 0u, 0u};
+    if (src >= 0 && h0 + hv < H)
+      in[e] = *reinterpret_cast<const u32x4_t*>(X + (int64_t)src * H + h0 + hv);
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int q = tid + e * 256;
+    const int r = q / VPR, hv = (q % VPR) * VE;
+    const S* v = reinterpret_cast<const S*>(&in[e]);
+#pragma unroll
+    for (int k = 0; k < VE; ++k) tile[r][hv + k] = v[k];
   }
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < PER; ++e) {
     const int q = tid + e * 256;
-    const int h = q >> 6, r = q & 63;
-    if (h0 + h < H && r0 + r < ldx) XcT[(h0 + h) * ldx + r0 + r] = tile[r][h];
+    const int h = q / VPR, rv = (q % VPR) * VE;
+    u32x4_t out;
+    S* o = reinterpret_cast<S*>(&out);
+#pragma unroll
+    for (int k = 0; k < VE; ++k) o[k] = tile[rv + k][h];
+    // ldx is a multiple of 8 (and so of VE): a vector lies wholly below or past it
+    if (h0 + h < H && r0 + rv < ldx)
+      *reinterpret_cast<u32x4_t*>(XcT + (h0 + h) * ldx + r0 + rv) = out;
   }
 }
 
