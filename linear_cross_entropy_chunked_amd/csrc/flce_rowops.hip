@@ -379,11 +379,18 @@ __global__ __launch_bounds__(256) void dx_reduce_kernel(DxReduceArgs a) {
        e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t f = e * 4;
     const int64_t m = f / a.H, n = f % a.H;
+    // Splits summed in order 0, 1, 2, ...; eight loads in flight at a time.
     f32x4_t acc = *reinterpret_cast<const f32x4_t*>(a.partial + f);
-    for (int sp = 1; sp < a.splits; ++sp) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.partial + sp * plane + f);
-      acc += v;
+    int sp = 1;
+    for (; sp + 8 <= a.splits; sp += 8) {
+      f32x4_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = *reinterpret_cast<const f32x4_t*>(a.partial + (sp + u) * plane + f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
     }
+    for (; sp < a.splits; ++sp) acc += *reinterpret_cast<const f32x4_t*>(a.partial + sp * plane + f);
     S* o = dX + (int64_t)a.idx[m] * a.H + n;
 #pragma unroll
     for (int q = 0; q < 4; ++q) o[q] = T::from_f32(s * acc[q]);
