@@ -964,7 +964,7 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
                                             int64_t m0, int n0, int64_t V, int H, float sc,
                                             bool accumulate) {
   typedef Stage<C> ST;
-  constexpr int LS = ST::LS, SUBS = ST::SUBS, NQ = ST::NQ;
+  constexpr int LS = ST::LS;
   constexpr bool F32 = std::is_same<D, float>::value;
   constexpr uint64_t ES = F32 ? 4 : 2;
   // The destination values are read through a buffer descriptor over this
@@ -976,23 +976,33 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
   const uint64_t span = (uint64_t)trows * (uint64_t)H * ES;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       static_cast<unsigned char*>(dW) + (uint64_t)m0 * (uint64_t)H * ES, 0, (int)span, 0x00020000);
+  // A piece is PC columns of one staged row, one 16-byte vector of dW: 4
+  // columns of an fp32 dW under the eight-wave tiles, 8 of a 16-bit one.
+  // Consecutive lanes then read and write consecutive 16-byte chunks of a
+  // row (chunk 2048: grad_weight 2.14 -> 2.07 ms against 8-column pieces of
+  // two vectors each, which the four-wave fp32 tiles keep: 4 % faster there).
+  constexpr bool ONE = !F32 || C::NT == 512;
+  constexpr int PC = F32 ? (ONE ? 4 : 8) : 8;
+  constexpr int NV = ONE ? 1 : 2;           // 16-byte vectors per piece
+  constexpr int SUBSP = C::BN / PC;         // pieces per staged row
+  constexpr int NQP = ST::ROWS * SUBSP / C::NT;
+  static_assert((ST::ROWS * SUBSP) % C::NT == 0, "uniform piece count per lane");
   for (int p = 0; p < ST::PASSES; ++p) {
-    u32x4_t old[NQ][F32 ? 2 : 1];
+    u32x4_t old[NQP * NV];
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int q = tid + i * C::NT, lrow = q / SUBS, piece = q % SUBS;
+    for (int i = 0; i < NQP; ++i) {
+      const int q = tid + i * C::NT, lrow = q / SUBSP, piece = q % SUBSP;
       const int64_t gm = m0 + p * ST::ROWS + lrow;
-      const int gn = n0 + piece * 8;
+      const int gn = n0 + piece * PC;
       const bool live = accumulate && gm < V && gn < H;
+      const uint32_t off =
+          live ? (uint32_t)(((uint64_t)(p * ST::ROWS + lrow) * (uint64_t)H + (uint64_t)gn) * ES)
+               : kOOB;
 #pragma unroll
-      for (int h = 0; h < (F32 ? 2 : 1); ++h) {
-        const uint32_t off =
-            live ? (uint32_t)(((uint64_t)(p * ST::ROWS + lrow) * (uint64_t)H + (uint64_t)gn) * ES) +
-                       16u * (uint32_t)h
-                 : kOOB;
-        old[i][h] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, F32 ? 0 : kNonTemporal));
-      }
+      for (int h = 0; h < NV; ++h)
+        old[i * NV + h] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off == kOOB ? kOOB : off + 16u * h),
+                                                           0, F32 ? 0 : kNonTemporal));
     }
     __syncthreads();
     if (wm / ST::WR == p) {
@@ -1010,23 +1020,25 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int q = tid + i * C::NT, lrow = q / SUBS, piece = q % SUBS;
+    for (int i = 0; i < NQP; ++i) {
+      const int q = tid + i * C::NT, lrow = q / SUBSP, piece = q % SUBSP;
       const int64_t gm = m0 + p * ST::ROWS + lrow;
-      const int gn = n0 + piece * 8;
+      const int gn = n0 + piece * PC;
       if (gm >= V || gn >= H) continue;
-      const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8);
-      const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8 + 4);
-      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       if constexpr (F32) {
-        f32x4_t* dst = reinterpret_cast<f32x4_t*>(static_cast<float*>(dW) + gm * H + gn);
-        const f32x4_t o0 = __builtin_bit_cast(f32x4_t, old[i][0]);
-        const f32x4_t o1 = __builtin_bit_cast(f32x4_t, old[i][1]);
-        dst[0] = f32x4_t{v[0] * sc + o0[0], v[1] * sc + o0[1], v[2] * sc + o0[2], v[3] * sc + o0[3]};
-        dst[1] = f32x4_t{v[4] * sc + o1[0], v[5] * sc + o1[1], v[6] * sc + o1[2], v[7] * sc + o1[3]};
+#pragma unroll
+        for (int h = 0; h < NV; ++h) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * PC + 4 * h);
+          const f32x4_t o = __builtin_bit_cast(f32x4_t, old[i * NV + h]);
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(dW) + gm * H + gn + 4 * h) =
+              f32x4_t{v[0] * sc + o[0], v[1] * sc + o[1], v[2] * sc + o[2], v[3] * sc + o[3]};
+        }
       } else {
+        const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8);
+        const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8 + 4);
+        float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         float o[8];
-        unpack8<D>(old[i][0], o);
+        unpack8<D>(old[i], o);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = v[e] * sc + o[e];
         __builtin_nontemporal_store(pack8<D>(v),
