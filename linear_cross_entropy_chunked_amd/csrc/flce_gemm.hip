@@ -946,7 +946,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void dx_kernel(DxArgs a) 
 // so those loads' latency overlaps the staging instead of serialising with
 // the stores (the compiler cannot move a load of one piece above the store
 // of another).
-// Cache policy of a buffer load: non-temporal (gfx950's nt bit).
+// Cache policy of a buffer load or store: non-temporal (gfx950's nt bit).
 constexpr int kNonTemporal = 2;
 
 // A 16-bit dW is read and written non-temporally.  Its read-modify-write is
@@ -967,15 +967,19 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
   constexpr int LS = ST::LS;
   constexpr bool F32 = std::is_same<D, float>::value;
   constexpr uint64_t ES = F32 ? 4 : 2;
-  // The destination values are read through a buffer descriptor over this
-  // tile's rows of dW: a piece outside the matrix (or every piece, when not
-  // accumulating) takes an offset past the range and reads zeros, so the loads
-  // need no branches and the compiler can wait for them one piece at a time.
-  // (The library limits H to 2^20, so a tile's rows span at most 1 GiB.)
+  // The destination values are read and written through buffer descriptors
+  // over this tile's rows of dW: a piece outside the matrix takes an offset
+  // past the range, so its load reads zeros and its store is dropped, and
+  // when not accumulating the load descriptor is empty.  The loads and
+  // stores then need no branches, and the compiler can wait for the loads
+  // one piece at a time.  (The library limits H to 2^20, so a tile's rows
+  // span at most 1 GiB.)
   const int64_t trows = V - m0 < C::BM ? V - m0 : C::BM;
   const uint64_t span = (uint64_t)trows * (uint64_t)H * ES;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      static_cast<unsigned char*>(dW) + (uint64_t)m0 * (uint64_t)H * ES, 0, (int)span, 0x00020000);
+  unsigned char* const base = static_cast<unsigned char*>(dW) + (uint64_t)m0 * (uint64_t)H * ES;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)span, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rl =
+      __builtin_amdgcn_make_buffer_rsrc(base, 0, accumulate ? (int)span : 0, 0x00020000);
   // A piece is PC columns of one staged row, one 16-byte vector of dW: 4
   // columns of an fp32 dW under the eight-wave tiles, 8 of a 16-bit one.
   // Consecutive lanes then read and write consecutive 16-byte chunks of a
@@ -986,52 +990,72 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
   constexpr int NV = ONE ? 1 : 2;           // 16-byte vectors per piece
   constexpr int SUBSP = C::BN / PC;         // pieces per staged row
   constexpr int NQP = ST::ROWS * SUBSP / C::NT;
-  static_assert((ST::ROWS * SUBSP) % C::NT == 0, "uniform piece count per lane");
-  for (int p = 0; p < ST::PASSES; ++p) {
+  static_assert((ST::ROWS * SUBSP) % C::NT == 0 && C::NT % SUBSP == 0, "uniform pieces per lane");
+  // With one workgroup per CU, pass p stages BAND rows of every wave (its
+  // accumulator blocks [p IPB, (p + 1) IPB)) rather than all rows of half
+  // the waves, so every wave writes half as much per staging step.
+  // Interleaved on MI355X: grad_weight at chunk 2048 2.107 -> 2.068 ms, at
+  // chunk 256 857 -> 788 us, bf16 dW at H 5376 / V 262144 1436 -> 1375 us.
+  // The tiles that share a CU between two workgroups keep rows of waves
+  // (masked SFT at chunk 128: 242 against 245 us).  Each pass's destination
+  // values are loaded at its start, before the barrier, and overlap the
+  // staging; loading the next pass's values before this pass's stores was
+  // no faster.
+  constexpr bool SPLIT = C::WGS == 1;
+  constexpr int PASSES = ST::PASSES, BAND = SPLIT ? ST::ROWS / C::WAVES_M : C::WTM, IPB = BAND / 32;
+  static_assert(BAND % 32 == 0 && (!SPLIT || PASSES * BAND == C::WTM), "whole blocks per pass");
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    // Byte offset of piece i of this thread, or kOOB for a piece past column
+    // H (a row past V lies past the descriptor's range by itself; a thread's
+    // pieces all have the same columns, since SUBSP divides NT).  Staged row
+    // s is tile row (s / BAND) WTM + p BAND + s % BAND when split, else
+    // p ROWS + s.
+    auto piece_off = [&](int i) -> uint32_t {
+      const int s = (tid + i * C::NT) / SUBSP, gn = n0 + (tid % SUBSP) * PC;
+      const int tr = SPLIT ? (s / BAND) * C::WTM + p * BAND + s % BAND : p * ST::ROWS + s;
+      return gn < H ? (uint32_t)(((uint64_t)tr * (uint64_t)H + (uint64_t)gn) * ES) : kOOB;
+    };
     u32x4_t old[NQP * NV];
 #pragma unroll
     for (int i = 0; i < NQP; ++i) {
-      const int q = tid + i * C::NT, lrow = q / SUBSP, piece = q % SUBSP;
-      const int64_t gm = m0 + p * ST::ROWS + lrow;
-      const int gn = n0 + piece * PC;
-      const bool live = accumulate && gm < V && gn < H;
-      const uint32_t off =
-          live ? (uint32_t)(((uint64_t)(p * ST::ROWS + lrow) * (uint64_t)H + (uint64_t)gn) * ES)
-               : kOOB;
+      const uint32_t off = piece_off(i);
 #pragma unroll
       for (int h = 0; h < NV; ++h)
         old[i * NV + h] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off == kOOB ? kOOB : off + 16u * h),
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rl, (int)(off == kOOB ? kOOB : off + 16u * h),
                                                            0, F32 ? 0 : kNonTemporal));
     }
     __syncthreads();
-    if (wm / ST::WR == p) {
-      const int r0 = (wm % ST::WR) * C::WTM;
+    if (SPLIT || wm / ST::WR == p) {
+      const int r0 = SPLIT ? wm * BAND : (wm % ST::WR) * C::WTM;
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
+        if (!SPLIT || i / IPB == p)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
+          for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = r0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            const int col = wn * C::WTN + j * 32 + (lane & 31);
-            stage[row * LS + col] = acc[i][j][r];
-          }
+            for (int r = 0; r < 16; ++r) {
+              const int row = r0 + (i % IPB) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+              const int col = wn * C::WTN + j * 32 + (lane & 31);
+              stage[row * LS + col] = acc[i][j][r];
+            }
     }
     __syncthreads();
+    // Stores go through the same descriptor, so a piece outside the matrix
+    // is dropped by the hardware and the loop has no branch.
 #pragma unroll
     for (int i = 0; i < NQP; ++i) {
       const int q = tid + i * C::NT, lrow = q / SUBSP, piece = q % SUBSP;
-      const int64_t gm = m0 + p * ST::ROWS + lrow;
-      const int gn = n0 + piece * PC;
-      if (gm >= V || gn >= H) continue;
+      const uint32_t off = piece_off(i);
       if constexpr (F32) {
 #pragma unroll
         for (int h = 0; h < NV; ++h) {
           const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * PC + 4 * h);
           const f32x4_t o = __builtin_bit_cast(f32x4_t, old[i * NV + h]);
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(dW) + gm * H + gn + 4 * h) =
-              f32x4_t{v[0] * sc + o[0], v[1] * sc + o[1], v[2] * sc + o[2], v[3] * sc + o[3]};
+          const f32x4_t w = {v[0] * sc + o[0], v[1] * sc + o[1], v[2] * sc + o[2], v[3] * sc + o[3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w), rs,
+                                                 (int)(off == kOOB ? kOOB : off + 16u * h), 0, 0);
         }
       } else {
         const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8);
@@ -1041,8 +1065,7 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
         unpack8<D>(old[i], o);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = v[e] * sc + o[e];
-        __builtin_nontemporal_store(pack8<D>(v),
-                                    reinterpret_cast<u32x4_t*>(static_cast<u16*>(dW) + gm * H + gn));
+        __builtin_amdgcn_raw_buffer_store_b128(pack8<D>(v), rs, (int)off, 0, kNonTemporal);
       }
     }
   }
