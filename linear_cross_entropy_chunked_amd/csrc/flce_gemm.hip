@@ -949,16 +949,25 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void dx_kernel(DxArgs a) 
 // Cache policy of a buffer load or store: non-temporal (gfx950's nt bit).
 constexpr int kNonTemporal = 2;
 
-// A 16-bit dW is read and written non-temporally.  Its read-modify-write is
-// the chunk's largest stream at small chunks (2 V H s bytes), and kept out of
-// the caches it no longer evicts the weight rows that grad_input has just
-// read: the next chunk's logits GEMM then finds part of W in the 256 MB
-// memory-side cache.  Measured on MI355X (loads and stores both
-// non-temporal; either alone gained nothing): masked SFT (V 151936, H 2048,
-// chunk 128) 42.8 -> 39.7 ms per step, logits 220 -> 179 us per chunk;
-// long sequences (V 262144, H 5376, chunk 256) 95.7 -> 93.4 ms.  An fp32 dW
-// stays cached: there the same change made grad_weight 1-3 % slower.
-template <class C, class D>
+// Under 16-bit operands dW is read and written non-temporally (NT).  Its
+// read-modify-write is the chunk's largest stream at small chunks (2 V H a
+// bytes), and kept out of the caches it no longer evicts the operand panels
+// that other tiles of the same XCD are about to read, nor the weight rows
+// that grad_input has just read: the next chunk's logits GEMM then finds
+// part of W in the 256 MB memory-side cache.  Measured on MI355X (loads and
+// stores both non-temporal; either alone gained nothing):
+//   16-bit dW: masked SFT (V 151936, H 2048, chunk 128) 42.8 -> 39.7 ms per
+//     step, logits 220 -> 179 us per chunk; long sequences (V 262144,
+//     H 5376, chunk 256) 95.7 -> 93.4 ms;
+//   fp32 dW, Llama shape: chunk 256 42.96 -> 40.15 ms per step (grad_weight
+//     792 -> 733 us, logits 283 -> 256 us); chunk 2048 grad_weight 2016 ->
+//     1997 us.  At chunk 2048 the cached read-modify-write of a tile had
+//     pushed the operand panels out of L2: the L2 issued about 36 M more
+//     read requests per launch than a launch that does not read dW, twice
+//     what reading dW itself takes.
+// With fp32 operands (a k loop 16 times as long) the hint made grad_weight
+// 1 % slower, and dW stays cached there.
+template <class C, class D, bool NT>
 __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[C::FM][C::FN],
                                             int wm, int wn, int lane, int tid, void* dW,
                                             int64_t m0, int n0, int64_t V, int H, float sc,
@@ -1024,7 +1033,7 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
       for (int h = 0; h < NV; ++h)
         old[i * NV + h] = __builtin_bit_cast(
             u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rl, (int)(off == kOOB ? kOOB : off + 16u * h),
-                                                           0, F32 ? 0 : kNonTemporal));
+                                                           0, NT ? kNonTemporal : 0));
     }
     __syncthreads();
     if (SPLIT || wm / ST::WR == p) {
@@ -1055,7 +1064,8 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
           const f32x4_t o = __builtin_bit_cast(f32x4_t, old[i * NV + h]);
           const f32x4_t w = {v[0] * sc + o[0], v[1] * sc + o[1], v[2] * sc + o[2], v[3] * sc + o[3]};
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w), rs,
-                                                 (int)(off == kOOB ? kOOB : off + 16u * h), 0, 0);
+                                                 (int)(off == kOOB ? kOOB : off + 16u * h), 0,
+                                                 NT ? kNonTemporal : 0);
         }
       } else {
         const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(stage + lrow * LS + piece * 8);
@@ -1065,7 +1075,7 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
         unpack8<D>(old[i], o);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = v[e] * sc + o[e];
-        __builtin_amdgcn_raw_buffer_store_b128(pack8<D>(v), rs, (int)off, 0, kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b128(pack8<D>(v), rs, (int)off, 0, NT ? kNonTemporal : 0);
       }
     }
   }
@@ -1124,8 +1134,8 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void dw_kernel(DwArgs a) 
 
   const float sc = upstream_scale(a.grad_output, a.inv_n, a.reduction);
   const bool accumulate = a.accumulate != 0;
-  dw_epilogue<C, D>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid, a.dW, m0, n0, a.V,
-                    H, sc, accumulate);
+  dw_epilogue<C, D, sizeof(S) == 2>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid, a.dW,
+                                    m0, n0, a.V, H, sc, accumulate);
 }
 
 // ---------------------------------------------------------------------------
