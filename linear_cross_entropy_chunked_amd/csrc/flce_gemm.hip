@@ -951,8 +951,7 @@ constexpr int kNonTemporal = 2;
 
 // Under 16-bit operands dW is read and written non-temporally (NT).  Its
 // read-modify-write is the chunk's largest stream at small chunks (2 V H a
-// bytes), and kept out of the caches it no longer evicts the operand panels
-// that other tiles of the same XCD are about to read, nor the weight rows
+// bytes), and kept out of the caches it no longer evicts the weight rows
 // that grad_input has just read: the next chunk's logits GEMM then finds
 // part of W in the 256 MB memory-side cache.  Measured on MI355X (loads and
 // stores both non-temporal; either alone gained nothing):
@@ -961,10 +960,7 @@ constexpr int kNonTemporal = 2;
 //     H 5376, chunk 256) 95.7 -> 93.4 ms;
 //   fp32 dW, Llama shape: chunk 256 42.96 -> 40.15 ms per step (grad_weight
 //     792 -> 733 us, logits 283 -> 256 us); chunk 2048 grad_weight 2016 ->
-//     1997 us.  At chunk 2048 the cached read-modify-write of a tile had
-//     pushed the operand panels out of L2: the L2 issued about 36 M more
-//     read requests per launch than a launch that does not read dW, twice
-//     what reading dW itself takes.
+//     1997 us.
 // With fp32 operands (a k loop 16 times as long) the hint made grad_weight
 // 1 % slower, and dW stays cached there.
 template <class C, class D, bool NT>
