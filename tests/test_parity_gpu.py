@@ -206,6 +206,27 @@ def test_accumulate_into_given_grad_weight(pkg):
     _check(r, ref, "f32", "sum")
 
 
+@pytest.mark.parametrize("dtype,accum,chunk", [
+    ("bf16", "f32", 128), ("bf16", "same", 128), ("f16", "f32", 128),  # 256 x 128, two per CU
+    ("bf16", "f32", 512), ("bf16", "same", 512), ("f16", "same", 512),  # eight-wave 256 x 256
+    ("f32", "f32", 64), ("f32", "f32", 512)])                            # four-wave fp32 tiles
+def test_accumulate_on_every_grad_weight_tile(pkg, dtype, accum, chunk):
+    """accumulate_dw adds to a given dW on each grad_weight tile and cache
+    policy (16-bit operands read and write dW non-temporally): the first chunk
+    reads the given values, the later chunks their own sums.  V = 1100 and
+    H = 392 are ragged against every tile."""
+    BT, H, V = 900, 392, 1100
+    seed = 2600 + chunk + len(dtype) + (accum == "f32")
+    X, W, t = si.make_case(BT, H, V, dtype, seed, ignore="scattered", frac=0.1)
+    init = torch.linspace(-0.05, 0.05, V * H, dtype=torch.float32).reshape(V, H)
+    init = init.to(TD[dtype] if accum == "same" else torch.float32)
+    r = _run(pkg, X, W, t, reduction="sum", chunk_size=chunk, dW_init=init,
+             accum_dtype=torch.float32 if accum == "f32" else None)
+    ref = oracle.flce(X, W, t, reduction="sum", dW_init=init)
+    assert r.stats["chunks_run"] == math.ceil(ref["n_valid"] / chunk) > 1
+    _check(r, ref, dtype, "sum")
+
+
 def test_frozen_weight(pkg):
     BT, H, V = 200, 128, 900
     X, W, t = si.make_case(BT, H, V, "bf16", 4003, ignore="prompt_first", frac=0.5, seq_len=100)
