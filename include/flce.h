@@ -111,7 +111,7 @@ int64_t flce_chunk_size(int64_t BT, int64_t H, int64_t V, int64_t chunk_size,
  *                the measured device-copy rate)
  *   chunk time = GEMM time + HBM time (the per-chunk weight traffic is not
  *                hidden behind the GEMMs: measured per-step times fit
- *                T(c) = T_inf + (BT / c) x 0.82 ms at BT 8192, H 4096,
+ *                T(c) = T_inf + (BT / c) x 0.60 ms at BT 8192, H 4096,
  *                V 128256)
  * s / a: operand / accumulation item sizes.  The logits slab is kept within
  * slab_budget_bytes (0: 2 GiB); the result is then floored to a power of two
