@@ -1047,8 +1047,9 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
             }
     }
     __syncthreads();
-    // Stores go through the same descriptor, so a piece outside the matrix
-    // is dropped by the hardware and the loop has no branch.
+    // Stores go through the tile's descriptor (rs, never empty), so a piece
+    // outside the matrix is dropped by the hardware and the loop has no
+    // branch.
 #pragma unroll
     for (int i = 0; i < NQP; ++i) {
       const int q = tid + i * C::NT, lrow = q / SUBSP, piece = q % SUBSP;
