@@ -19,11 +19,11 @@
 // Tile shapes: 256x256 blocks (one workgroup per CU) of four 128x128 waves
 // for fp32 operands and of eight 64x128 or 128x64 waves (two per SIMD) for
 // 16-bit operands; for chunks of at most 128 rows with 16-bit operands,
-// 128x128 logits blocks of eight 64x32 waves over 256-byte k rows and
-// 128x256 grad_input blocks of eight 64x64 waves and 256x128 grad_weight
-// blocks of eight 64x64 waves, two workgroups per CU; 128x128 blocks of four
-// 64x64 waves (two workgroups per CU) for the other small problems (fp32
-// with few rows, or fewer than 256 hidden units).
+// 128x128 logits blocks of eight 64x32 waves (two workgroups per CU),
+// 128x256 grad_input blocks of eight 64x64 waves (one per CU) and 256x128
+// grad_weight blocks of eight 64x64 waves (two per CU); 128x128 blocks of
+// four 64x64 waves (two workgroups per CU) for the other small problems
+// (fp32 with few rows, or fewer than 256 hidden units).
 #include <type_traits>
 
 #include "flce_device.hpp"
@@ -56,7 +56,7 @@ typedef Cfg<256, 256, 128, 1> Big;         // 4 waves of 128 x 128 (fp32 operand
 typedef Cfg<256, 256, 128, 1, 4, 2> Big8M;  // 8 waves of 64 x 128 (16-bit logits, grad_weight)
 typedef Cfg<256, 256, 128, 1, 2, 4> Big8N;  // 8 waves of 128 x 64 (16-bit grad_input)
 typedef Cfg<128, 128, 128, 2> Small;        // 4 waves of 64 x 64, 2 workgroups per CU
-typedef Cfg<128, 128, 256, 1, 2, 4> SmallK; // 8 waves of 64 x 32, 256-byte k rows (16-bit logits, <= 128 rows)
+typedef Cfg<128, 128, 128, 2, 2, 4> Small8; // 8 waves of 64 x 32, 2 workgroups per CU (16-bit logits, <= 128 rows)
 typedef Cfg<128, 256, 128, 1, 2, 4> Mid8N;  // 8 waves of 64 x 64 (16-bit grad_input, <= 128 rows)
 typedef Cfg<256, 128, 64, 2, 4, 2> Twin8M;  // 8 waves of 64 x 64, 2 workgroups per CU (16-bit grad_weight, <= 128 rows)
 
@@ -67,7 +67,7 @@ typedef Cfg<256, 128, 64, 2, 4, 2> Twin8M;  // 8 waves of 64 x 64, 2 workgroups 
 // tile's loads over the k-steps of the previous tile's MFMA work.
 template <class C> struct LogitsPipe { static constexpr int SA = 2, SB = 3, P = 2; };
 template <> struct LogitsPipe<Big8M> { static constexpr int SA = 2, SB = 3, P = 1; };
-template <> struct LogitsPipe<SmallK> { static constexpr int SA = 2, SB = 3, P = 1; };
+template <> struct LogitsPipe<Small8> { static constexpr int SA = 2, SB = 3, P = 1; };
 template <class C> struct DxPipe { static constexpr int SA = 3, SB = 2, P = 2; };
 // grad_input with the eight-wave tile (chunks of more than 128 rows): three
 // stages of G, two of W.  Measured interleaved against two of G and three of
@@ -171,15 +171,12 @@ template <class T, int RB_>
 struct RowSwz {
   typedef typename T::storage S;
   static constexpr int RB = RB_;
-  static_assert(RB == 64 || RB == 128 || RB == 256, "row swizzle assumes 64-, 128- or 256-byte rows");
+  static_assert(RB == 64 || RB == 128, "row swizzle assumes 64- or 128-byte rows");
   static constexpr size_t bytes(int R) { return (size_t)R * RB; }
   // LDS serves 256 bytes per cycle (64 banks): the 16 rows read by 16
   // consecutive lanes must land in 16 distinct 16-byte slots of that window.
-  // 256-byte rows: chunk ^= r % 16; 128-byte rows: chunk ^= (r / 2) % 8;
-  // 64-byte rows: chunk ^= (r / 4) % 4.
-  __device__ __forceinline__ static int swz(int r) {
-    return RB == 256 ? (r & 15) : RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
-  }
+  // 128-byte rows: chunk ^= (r / 2) % 8; 64-byte rows: chunk ^= (r / 4) % 4.
+  __device__ __forceinline__ static int swz(int r) { return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
   __device__ __forceinline__ static u32x4_t frag16(const unsigned char* b, int r, int s, int lane) {
     const int kc = 2 * s + (lane >> 5);
     return *reinterpret_cast<const u32x4_t*>(b + r * RB + ((kc ^ swz(r)) << 4));
@@ -1199,10 +1196,13 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t st) {
 // 0.95 -> 0.89 ms with fp32 dW, 2.24 -> 1.72 ms with bf16 dW at H 5376,
 // V 262144; at chunk 128 both GEMMs 9-12 % faster).  Logits keep a
 // 128 x 128 tile for chunks of at most 128 rows (7-11 % faster there than
-// 256 x 256); with 16-bit operands it is eight waves over k-tiles of 256
-// bytes per row (one workgroup per CU), whose longer runs per W row the
-// memory streams faster at H 2048 (masked SFT chunk 128: 174.6 -> 170.9 us
-// trained, 166.6 -> 161.7 us frozen per launch).
+// 256 x 256); with 16-bit operands it is eight waves, two workgroups per CU,
+// so that one workgroup's first loads and epilogue overlap the other's k
+// loop.  Interleaved against one workgroup per CU over 256-byte k rows
+// (longer runs per W row, but each tile's pipeline fill exposed): masked SFT
+// (H 2048) at chunk 128 175 -> 169 us trained, 162 -> 161 us frozen; the
+// Llama shape at chunk 128 227 -> 219 us.  Splitting each k-tile's loads in
+// two parts was slower (176 us).
 enum class Shape { Small, Big };
 Shape logits_shape(int rows, int64_t V) { return rows > 128 && V >= 1024 ? Shape::Big : Shape::Small; }
 Shape dx_shape(int rows, int64_t H, bool wide) {
@@ -1216,7 +1216,7 @@ template <class T>
 static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
   constexpr bool k16 = sizeof(typename T::storage) == 2;
   typedef typename std::conditional<k16, Big8M, Big>::type L;
-  typedef typename std::conditional<k16, SmallK, Small>::type LS;
+  typedef typename std::conditional<k16, Small8, Small>::type LS;
   return logits_shape(a.rows, a.V) == Shape::Big ? launch_logits_t<T, L>(a, st)
                                                  : launch_logits_t<T, LS>(a, st);
 }
@@ -1267,7 +1267,7 @@ DxTile dx_tile(int dtype, int rows, int64_t H) {
 // Column width of one (max, sum exp) entry written by the logits GEMM.
 int stats_cols() {
   static_assert(Big::BN % 64 == 0 && Big8M::BN % 64 == 0 && Small::BN % 64 == 0 &&
-                    SmallK::BN % 64 == 0,
+                    Small8::BN % 64 == 0,
                 "64-column stats blocks");
   return 64;
 }
