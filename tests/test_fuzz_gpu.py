@@ -12,6 +12,10 @@ gradient.  The oracle sees the clean inputs; the HIP path must not notice the
 NaN.  Tolerances as everywhere: fp32 loss 1e-5 and gradients 1e-4; 16-bit
 loss 2e-3 and gradients 2e-2 (relative, Frobenius).  The labelled-row count
 and every ignored-row output are exact.
+
+A second generator draws larger shapes (BT 257-1499, H 192-512, V 1025-2999,
+chunks of 256-1024 rows), which run the eight-wave 256 x 256 tiles of all three
+GEMMs with ragged edges and several chunks per call.
 """
 import numpy as np
 import pytest
@@ -61,6 +65,27 @@ def draw(i):
                 seed=5000 + 17 * i)
 
 
+# cases 0-11 and four that accumulate into a given dW (16, 17, 22, 38)
+LARGE_CASES = list(range(12)) + [16, 17, 22, 38]
+
+
+def draw_large(i):
+    """Case i of the larger shapes (a pure function of i)."""
+    r = np.random.Generator(np.random.PCG64(777000 + i))
+    pick = lambda xs: xs[int(r.integers(len(xs)))]
+    dtype = pick(["f32", "bf16", "bf16", "f16"])
+    BT = int(r.integers(257, 1500))
+    H = 8 * int(r.integers(24, 65))
+    V = int(r.integers(1025, 3000))
+    chunk = pick([256, 300, 512, 640, 1024, None])
+    return dict(dtype=dtype, BT=BT, H=H, V=V, chunk=chunk, accum=pick(["f32", "same"]),
+                reduction=pick(["mean", "sum", "none"]), frozen=bool(r.random() < 0.1),
+                accumulate=bool(r.random() < 0.3),
+                ignore=pick(["none", "scattered", "prompt_first"]),
+                frac=float(pick([0.1, 0.5])), ignore_index=-100, poison=bool(r.random() < 0.5),
+                scalar=float(pick([1.0, 0.5])), mem_const=1, seed=70000 + 13 * i)
+
+
 @pytest.fixture(scope="module")
 def pkg(flce_lib):
     if not torch.cuda.is_available():
@@ -77,7 +102,15 @@ def _rel(a, b):
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_configuration(pkg, i):
-    c = draw(i)
+    _run_case(pkg, i, draw(i))
+
+
+@pytest.mark.parametrize("i", LARGE_CASES)
+def test_random_large_configuration(pkg, i):
+    _run_case(pkg, i, draw_large(i))
+
+
+def _run_case(pkg, i, c):
     dt, BT, H, V, ii = c["dtype"], c["BT"], c["H"], c["V"], c["ignore_index"]
     print(f"case {i}: {c}", flush=True)
     X = si.make_x(BT, H, dt, c["seed"])
