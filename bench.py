@@ -386,12 +386,12 @@ def roofline(res, cfg):
     if flops and flops / (peak_f * 1e12) >= byts / (HBM_PEAK_GBS * 1e9):
         achieved = flops / sec / 1e12
         return dict(kernel=name, bound="mfma", achieved=achieved, peak=peak_f, unit="TFLOP/s",
-                    frac=achieved / peak_f, traffic=None,
+                    frac=achieved / peak_f, traffic=None, rows_per_launch=rows,
                     hbm_frac_of_algorithmic_bytes=byts / sec / 1e9 / HBM_PEAK_GBS,
                     work_per_launch=f"2*c*H*V flops = {flops:.4g} (c={rows:g} rows on average)")
     achieved = byts / sec / 1e9
     out = dict(kernel=name, bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-               frac=achieved / HBM_PEAK_GBS, traffic=None,
+               frac=achieved / HBM_PEAK_GBS, traffic=None, rows_per_launch=rows,
                work_per_launch=f"algorithmic bytes = {byts:.4g} (c={rows:g} rows on average)")
     if flops:
         out["mfma_frac"] = flops / sec / 1e12 / peak_f
@@ -408,9 +408,9 @@ def ceilings(dev):
     import ctypes
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "linear_cross_entropy_chunked_amd", "libflce_probe.so"))
-    lib.flce_probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                         ctypes.c_void_p]
+    for f in (lib.flce_probe_mfma_loop, lib.flce_probe_mfma16_loop):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.flce_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     st = torch.cuda.current_stream(dev)
@@ -434,13 +434,15 @@ def ceilings(dev):
     sink = torch.empty(blocks * lib.flce_probe_mfma_threads(), dtype=torch.float32, device=dev)
     gen = torch.Generator().manual_seed(20240611)
     rnd = (torch.randn(8 << 20, generator=gen) * 0.05).to(torch.bfloat16).to(dev)
-    flops = blocks * 8 * iters * 32 * 2 * 32 * 32 * 16
+    flops = blocks * 8 * iters * 32 * 2 * 32 * 32 * 16  # the same for both shapes
     out = {}
-    for kind, ops in (("random", rnd), ("zero", torch.zeros_like(rnd))):
-        sec = timed(lambda: check(lib.flce_probe_mfma_loop(
-            ops.data_ptr(), ops.numel() * 2, sink.data_ptr(), sink.numel(), blocks, iters,
-            st.cuda_stream), "flce_probe_mfma_loop"), 12)
-        out[f"mfma_loop_bf16_{kind}_tflops"] = flops / sec / 1e12
+    for loop, key in ((lib.flce_probe_mfma_loop, "mfma_loop"),
+                      (lib.flce_probe_mfma16_loop, "mfma16_loop")):
+        for kind, ops in (("random", rnd), ("zero", torch.zeros_like(rnd))):
+            sec = timed(lambda: check(loop(
+                ops.data_ptr(), ops.numel() * 2, sink.data_ptr(), sink.numel(), blocks, iters,
+                st.cuda_stream), key), 12)
+            out[f"{key}_bf16_{kind}_tflops"] = flops / sec / 1e12
     del rnd, sink
     nbytes = 2 << 30
     sblocks = nbytes >> 20  # 1 MiB per workgroup
@@ -459,7 +461,8 @@ def ceilings(dev):
     del a, b
     torch.cuda.empty_cache()
     out["how"] = (f"probe library: {blocks} workgroups x 8 waves x {iters} iterations of 32 "
-                  f"independent v_mfma_f32_32x32x16_bf16 on register operands (random: "
+                  f"independent v_mfma_f32_32x32x16_bf16 (mfma16: 64 of "
+                  f"v_mfma_f32_16x16x32_bf16) on register operands (random: "
                   f"N(0, 0.05) in bf16; zero: all zero), timed over 12 launches; a read of "
                   f"2 GiB in {sblocks} contiguous 1 MiB segments, one per workgroup of 256, "
                   f"16 B per lane, 4 loads in flight per lane, over 10 launches; torch copy "
@@ -467,13 +470,22 @@ def ceilings(dev):
     return out
 
 
+# 16-bit grad_input launches of at least this many rows run on 16x16x32 MFMAs
+# (kDxSub16Rows in flce_gemm.hip); every other 16-bit GEMM on 32x32x16.
+DX_SUB16_ROWS = 1024
+
+
 def add_ceiling(rl, ceil, dtype):
-    """The dominant kernel's rate against what the chip sustains by itself."""
+    """The dominant kernel's rate against what the chip sustains by itself: the
+    MFMA loop of the shape the kernel runs on (chosen by the average rows per
+    launch), or the HBM read stream."""
     if not ceil:
         return
     if rl["bound"] == "mfma" and dtype in ("bf16", "f16"):
-        c = ceil["mfma_loop_bf16_random_tflops"]
-        rl["ceiling"] = dict(value=c, unit="TFLOP/s", kind="bf16 MFMA loop, random operands")
+        sub16 = rl.get("kernel") == "dx_gemm" and rl.get("rows_per_launch", 0) >= DX_SUB16_ROWS
+        key, shape = ("mfma16_loop", "16x16x32") if sub16 else ("mfma_loop", "32x32x16")
+        c = ceil[f"{key}_bf16_random_tflops"]
+        rl["ceiling"] = dict(value=c, unit="TFLOP/s", kind=f"bf16 {shape} MFMA loop, random operands")
         rl["frac_of_ceiling"] = rl["achieved"] / c
     elif rl["bound"] == "hbm":
         c = ceil["hbm_read_stream_gbs"]

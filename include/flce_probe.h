@@ -29,6 +29,13 @@ extern "C" {
 int flce_probe_mfma_loop(const void* operands, int64_t operand_bytes, float* sink,
                          int64_t sink_floats, int blocks, int iters, void* stream);
 
+/* The same loop with v_mfma_f32_16x16x32_bf16: each iteration runs 64
+ * independent 16x16x32 MFMAs (16 accumulators), the same flops as one
+ * iteration above, from the same operand fragments; arguments, sink and
+ * return codes as for flce_probe_mfma_loop. */
+int flce_probe_mfma16_loop(const void* operands, int64_t operand_bytes, float* sink,
+                           int64_t sink_floats, int blocks, int iters, void* stream);
+
 /* A read of `bytes` bytes of `src` (a multiple of 16) by `blocks` workgroups
  * of flce_probe_stream_threads() threads; workgroup b reads the b-th of
  * `blocks` contiguous segments (about 1 MiB each is what the benchmark uses),

@@ -177,8 +177,12 @@ struct RowSwz {
   // consecutive lanes must land in 16 distinct 16-byte slots of that window.
   // 128-byte rows: chunk ^= (r / 2) % 8; 64-byte rows: chunk ^= (r / 4) % 4.
   __device__ __forceinline__ static int swz(int r) { return RB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+  // Rows per 16-bit fragment read: 32 for 32x32x16 MFMAs, 16 for 16x16x32.
+  static constexpr int FRAG_ROWS = T::sub16 ? 16 : 32;
+  // 16-bit fragment of row r for k-step s: lane l takes the 16-byte chunk
+  // 2 s + l / 32 (32x32x16) or 4 s + l / 16 (16x16x32), 8 consecutive k.
   __device__ __forceinline__ static u32x4_t frag16(const unsigned char* b, int r, int s, int lane) {
-    const int kc = 2 * s + (lane >> 5);
+    const int kc = T::sub16 ? 4 * s + (lane >> 4) : 2 * s + (lane >> 5);
     return *reinterpret_cast<const u32x4_t*>(b + r * RB + ((kc ^ swz(r)) << 4));
   }
   __device__ __forceinline__ static float frag4(const unsigned char* b, int r, int k) {
@@ -193,17 +197,26 @@ struct ColSwz {
   static constexpr int EPC = 16 / (int)sizeof(S); // elements per 16-byte chunk
   static constexpr size_t bytes(int) { return (size_t)BK * RBT; }
   // 16-bit: the 4 k-rows of one transposing read move by 64 bytes each
-  // (chunk ^= 4 (k % 4)); fp32: odd k-rows move by 128 bytes (chunk ^= 8 (k % 2)).
+  // (chunk ^= 4 (k % 4)); for 16x16x32 fragments, whose second lane group
+  // reads k-rows 8 further on in the same pass, those move by another 32
+  // bytes (chunk ^= 2 ((k / 8) % 2)).  fp32: odd k-rows move by 128 bytes
+  // (chunk ^= 8 (k % 2)).
   static_assert(RBT >= 256, "column swizzle needs 16 chunks per k-row");
-  __device__ __forceinline__ static int swz(int k) { return sizeof(S) == 2 ? 4 * (k & 3) : 8 * (k & 1); }
+  __device__ __forceinline__ static int swz(int k) {
+    if constexpr (sizeof(S) == 4) return 8 * (k & 1);
+    return T::sub16 ? (4 * (k & 3)) ^ (2 * ((k >> 3) & 1)) : 4 * (k & 3);
+  }
   __device__ __forceinline__ static const unsigned char* at(const unsigned char* b, int k, int c) {
     return b + k * RBT + (((c / EPC) ^ swz(k)) << 4) + (c % EPC) * (int)sizeof(S);
   }
-  // c: first column of the 32-column MFMA block
+  // c: first column of the MFMA block (32 columns for 32x32x16, 16 for
+  // 16x16x32).  32x32x16: lanes 16-31 take the block's second 16 columns and
+  // lanes 32-63 k-rows 8 further on; 16x16x32: lane group g = l / 16 gathers
+  // k-rows 32 s + 8 g + 0..7.
   __device__ __forceinline__ static u32x4_t frag16(const unsigned char* b, int c, int s, int lane) {
     const int q = lane & 15;
-    const int col = c + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
-    const int k1 = 16 * s + 8 * (lane >> 5) + (q >> 2);
+    const int col = T::sub16 ? c + 4 * (q & 3) : c + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
+    const int k1 = T::sub16 ? 32 * s + 8 * (lane >> 4) + (q >> 2) : 16 * s + 8 * (lane >> 5) + (q >> 2);
     const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) v4i16_t*)at(b, k1, col));
     const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -351,7 +364,7 @@ struct Smem {
 };
 
 // Fragment address helpers: a RowSwz operand is addressed by its row, a
-// ColSwz operand by the first column of the 32-wide MFMA block.
+// ColSwz operand by the first column of the MFMA block (32 or 16 wide).
 template <class L> struct IsCol { static constexpr bool value = false; };
 template <class T, int R, int BK> struct IsCol<ColSwz<T, R, BK>> { static constexpr bool value = true; };
 
@@ -360,7 +373,7 @@ __device__ __forceinline__ u32x4_t frag16_of(const unsigned char* b, int blk, in
   if constexpr (IsCol<L>::value)
     return L::frag16(b, blk, s, lane);
   else
-    return L::frag16(b, blk + (lane & 31), s, lane);
+    return L::frag16(b, blk + (lane & (L::FRAG_ROWS - 1)), s, lane);
 }
 template <class L>
 __device__ __forceinline__ float frag4_of(const unsigned char* b, int blk, int s, int lane) {
@@ -368,9 +381,11 @@ __device__ __forceinline__ float frag4_of(const unsigned char* b, int blk, int s
 }
 
 // ---------------------------------------------------------------------------
-// One k-tile of the wave's tile from LDS.  Fragments are double buffered
-// across the MFMA k-steps: the LDS reads of step s+1 are issued before the
-// MFMAs of step s, and the interleave is pinned for the scheduler.
+// One k-tile of the wave's tile from LDS.  With 32x32 MFMAs fragments are
+// double buffered across the k-steps: the LDS reads of step s+1 are issued
+// before the MFMAs of step s, and the interleave is pinned for the
+// scheduler.  With 16x16x32 MFMAs (Mfma16) each step reads its own
+// fragments first.
 // ---------------------------------------------------------------------------
 // Scheduling groups: NR LDS reads (mask 0x100) spread evenly between NM
 // MFMAs (mask 0x008), read q followed by its share of MFMAs.
@@ -393,7 +408,37 @@ __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned
                                          int wm, int wn, int lane,
                                          f32x16_t (&acc)[C::FM][C::FN], DMA dma) {
   constexpr int STEPS = KT<T, C>::STEPS;
-  if constexpr (sizeof(typename T::storage) == 2) {
+  if constexpr (T::sub16) {
+    // 16x16x32 MFMAs: each 32x32 accumulator block is four 16x16 sub-blocks
+    // and a k-step covers 32 k.  A step's fragments (one 16-byte read per 16
+    // rows of a RowSwz operand, two transposing reads per 16 columns of a
+    // ColSwz one) are read at its start: double buffering them across steps
+    // needs twice the registers, and with the reads and MFMAs interleaved by
+    // the same pinning as below it was 7 % slower (grad_input at chunk 2048,
+    // 1632 -> 1861 us per launch).
+    u32x4_t fa[C::FM][2], fb[C::FN][2];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) fa[i][h] = frag16_of<LA>(Ab, wm * C::WTM + i * 32 + h * 16, s, lane);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) fb[j][h] = frag16_of<LB>(Bb, wn * C::WTN + j * 32 + h * 16, s, lane);
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          T::template mma16<0>(fa[i][0], fb[j][0], acc[i][j]);
+          T::template mma16<1>(fa[i][0], fb[j][1], acc[i][j]);
+          T::template mma16<2>(fa[i][1], fb[j][0], acc[i][j]);
+          T::template mma16<3>(fa[i][1], fb[j][1], acc[i][j]);
+        }
+      dma(s);
+    }
+  } else if constexpr (sizeof(typename T::storage) == 2) {
     u32x4_t fa[2][C::FM], fb[2][C::FN];
     auto fetch = [&](int buf, int s) {
 #pragma unroll
@@ -522,6 +567,18 @@ __device__ __forceinline__ void main_loop(IA ia, IB ib, int nk, unsigned char* s
   wait_and_barrier<0>();
 }
 
+// Row and column, within its 32x32 accumulator block, of element r of this
+// lane's accumulators: four 16x16 sub-blocks for 16x16x32 MFMAs (SUB16),
+// the 32x32 layout otherwise.
+template <bool SUB16>
+__device__ __forceinline__ int acc_row(int r, int lane) {
+  return SUB16 ? 16 * (r >> 3) + 4 * ((lane >> 4) & 3) + (r & 3) : 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+template <bool SUB16>
+__device__ __forceinline__ int acc_col(int r, int lane) {
+  return SUB16 ? 16 * ((r >> 2) & 1) + (lane & 15) : (lane & 31);
+}
+
 template <class C>
 __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::FM][C::FN]) {
 #pragma unroll
@@ -551,7 +608,7 @@ struct Stage {
   static_assert((ROWS * SUBS) % C::NT == 0, "uniform piece count per lane");
 };
 
-template <class C, class Fn>
+template <class C, bool SUB16, class Fn>
 __device__ __forceinline__ void staged_epilogue(float* stage, const f32x16_t (&acc)[C::FM][C::FN],
                                                 int wm, int wn, int lane, int tid, Fn fn) {
   typedef Stage<C> ST;
@@ -566,8 +623,8 @@ __device__ __forceinline__ void staged_epilogue(float* stage, const f32x16_t (&a
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row = r0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            const int col = wn * C::WTN + j * 32 + (lane & 31);
+            const int row = r0 + i * 32 + acc_row<SUB16>(r, lane);
+            const int col = wn * C::WTN + j * 32 + acc_col<SUB16>(r, lane);
             stage[row * LS + col] = acc[i][j][r];
           }
     }
@@ -593,7 +650,7 @@ __device__ __forceinline__ u32x4_t pack8(const float (&v)[8]) {
   u32x4_t o;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    if constexpr (std::is_same<T, BF16>::value)
+    if constexpr (std::is_same<typename T::base, BF16>::value)
       o[e] = f32x2_to_bf16x2(v[2 * e], v[2 * e + 1]);
     else
       o[e] = (uint32_t)T::from_f32(v[2 * e]) | ((uint32_t)T::from_f32(v[2 * e + 1]) << 16);
@@ -776,7 +833,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void logits_kernel(Logits
   S* slab = static_cast<S*>(a.slab);
   float2* stats = reinterpret_cast<float2*>(a.stats);
   const S* bias = static_cast<const S*>(a.bias);
-  staged_epilogue<C>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
+  staged_epilogue<C, T::sub16>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
                      [&](int brow, int bcol, float (&v)[8]) __attribute__((always_inline)) {
     // Branch-free except where a piece straddles the end of the vocabulary:
     // columns past V are masked to -inf for the statistics by selects.
@@ -916,7 +973,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void dx_kernel(DxArgs a) 
   S* dX = static_cast<S*>(a.dX);
   float* part = a.partial + (int64_t)split * a.rows_cap * H;
   const bool direct = a.splits == 1;
-  staged_epilogue<C>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
+  staged_epilogue<C, T::sub16>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid,
                      [&](int brow, int bcol, float (&v)[8]) __attribute__((always_inline)) {
     const int gm = m0 + brow;
     const int gn = n0 + bcol;
@@ -960,7 +1017,7 @@ constexpr int kNonTemporal = 2;
 //     1997 us.
 // With fp32 operands (a k loop 16 times as long) the hint made grad_weight
 // 1 % slower, and dW stays cached there.
-template <class C, class D, bool NT>
+template <class C, class D, bool NT, bool SUB16>
 __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[C::FM][C::FN],
                                             int wm, int wn, int lane, int tid, void* dW,
                                             int64_t m0, int n0, int64_t V, int H, float sc,
@@ -1038,8 +1095,8 @@ __device__ __forceinline__ void dw_epilogue(float* stage, const f32x16_t (&acc)[
           for (int j = 0; j < C::FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int row = r0 + (i % IPB) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-              const int col = wn * C::WTN + j * 32 + (lane & 31);
+              const int row = r0 + (i % IPB) * 32 + acc_row<SUB16>(r, lane);
+              const int col = wn * C::WTN + j * 32 + acc_col<SUB16>(r, lane);
               stage[row * LS + col] = acc[i][j][r];
             }
     }
@@ -1128,7 +1185,7 @@ __global__ __launch_bounds__(C::NT, C::WAVES_PER_SIMD) void dw_kernel(DwArgs a) 
 
   const float sc = upstream_scale(a.grad_output, a.inv_n, a.reduction);
   const bool accumulate = a.accumulate != 0;
-  dw_epilogue<C, D, sizeof(S) == 2>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid, a.dW,
+  dw_epilogue<C, D, sizeof(S) == 2, T::sub16>(reinterpret_cast<float*>(smem_raw), acc, wm, wn, lane, tid, a.dW,
                                     m0, n0, a.V, H, sc, accumulate);
 }
 
@@ -1220,15 +1277,28 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
   return logits_shape(a.rows, a.V) == Shape::Big ? launch_logits_t<T, L>(a, st)
                                                  : launch_logits_t<T, LS>(a, st);
 }
+// grad_input of chunks of at least kDxSub16Rows rows (16-bit operands) runs
+// on 16x16x32 MFMAs, which the power limit lets run at a higher clock where
+// the kernel is MFMA-bound.  Per launch, interleaved against 32x32x16 on the
+// Llama shape: chunk 256 258 -> 262 us, 512 and 1024 equal, 2048 1738 ->
+// 1691 us, 4096 3438 -> 3226 us; H 4096 / V 32000 with 16384 rows 451 ->
+// 425 us (bf16), 476 -> 433 us (fp16).  With few rows the kernel streams W
+// and the extra LDS reads of the 16x16 fragments cost more than they gain.
+// The logits and grad_weight GEMMs measured no gain (grad_weight at chunk
+// 2048 was 2 % slower) and keep 32x32x16.
+constexpr int kDxSub16Rows = 1024;
 template <class T>
 static hipError_t dx_t(const DxArgs& a, hipStream_t st) {
   constexpr bool k16 = sizeof(typename T::storage) == 2;
   typedef typename std::conditional<k16, Big8N, Big>::type L;
   if (dx_shape(a.rows, a.H, k16) != Shape::Big) return launch_dx_t<T, Small>(a, st);
-  if constexpr (k16)
-    return a.rows > 128 ? launch_dx_t<T, L, DxPipeG3>(a, st) : launch_dx_t<T, Mid8N>(a, st);
-  else
+  if constexpr (k16) {
+    if (a.rows <= 128) return launch_dx_t<T, Mid8N>(a, st);
+    return a.rows >= kDxSub16Rows ? launch_dx_t<Mfma16<T>, L, DxPipeG3>(a, st)
+                                  : launch_dx_t<T, L, DxPipeG3>(a, st);
+  } else {
     return launch_dx_t<T, L>(a, st);
+  }
 }
 template <class T, class D>
 static hipError_t dw_t(const DwArgs& a, hipStream_t st) {

@@ -7,6 +7,8 @@
 //                          With random operands the multipliers toggle as in
 //                          a real GEMM and the chip's power limit sets the
 //                          clock; with zero operands it does not.
+//   flce_probe_mfma16_loop the same with bf16 16x16x32 MFMAs, twice as many
+//                          per iteration (the same flops).
 //   flce_probe_read_stream a read of one large buffer in contiguous segments,
 //                          one per workgroup, 16 bytes per lane, four loads in
 //                          flight per lane: the HBM read rate.
@@ -20,6 +22,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kMfmaThreads = 512;   // eight waves: one workgroup per CU, two waves per SIMD
 constexpr int kStreamThreads = 256;
@@ -61,6 +64,41 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_loop_kernel(const u32x4_t* 
   sink[t] = s;
 }
 
+// The same operand rotation with 16x16x32 MFMAs: sixteen accumulators of four
+// floats, 64 MFMAs of 16384 flops per iteration.
+__global__ __launch_bounds__(kMfmaThreads) void mfma16_loop_kernel(const u32x4_t* __restrict__ ops,
+                                                                   int64_t nops, float* sink,
+                                                                   int iters) {
+  const int64_t t = (int64_t)blockIdx.x * kMfmaThreads + threadIdx.x;
+  u32x4_t a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = ops[(t * 8 + i) % nops];
+    b[i] = ops[(t * 8 + 4 + i) % nops];
+  }
+  f32x4_t acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = f32x4_t{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[(s + j) & 3]),
+                                                         __builtin_bit_cast(bf16x8_t, b[(s + 3 * j) & 3]),
+                                                         acc[j], 0, 0, 0);
+    const u32x4_t x = a[0];
+    a[0] = a[1]; a[1] = a[2]; a[2] = a[3]; a[3] = b[0];
+    b[0] = b[1]; b[1] = b[2]; b[2] = b[3]; b[3] = x;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += acc[j][e];
+  sink[t] = s;
+}
+
 // Workgroup b reads the b-th of gridDim.x contiguous segments, four 16-byte
 // loads in flight per lane (contiguous segments of about 1 MiB measured
 // faster than a grid-strided sweep of the whole buffer: 5.9 against 5.3 TB/s).
@@ -88,6 +126,16 @@ extern "C" int flce_probe_mfma_loop(const void* operands, int64_t operand_bytes,
       sink_floats < (int64_t)blocks * kMfmaThreads)
     return 1;
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(kMfmaThreads), 0, (hipStream_t)stream,
+                     (const u32x4_t*)operands, operand_bytes / 16, sink, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+extern "C" int flce_probe_mfma16_loop(const void* operands, int64_t operand_bytes, float* sink,
+                                      int64_t sink_floats, int blocks, int iters, void* stream) {
+  if (!operands || !sink || operand_bytes < 16 || blocks <= 0 || iters < 0 ||
+      sink_floats < (int64_t)blocks * kMfmaThreads)
+    return 1;
+  hipLaunchKernelGGL(mfma16_loop_kernel, dim3(blocks), dim3(kMfmaThreads), 0, (hipStream_t)stream,
                      (const u32x4_t*)operands, operand_bytes / 16, sink, iters);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

@@ -45,7 +45,7 @@ def test_probe_library_exports_its_header(flce_lib):
     import subprocess
     path = os.path.join(os.path.dirname(flce_lib.LIB_PATH), "libflce_probe.so")
     declared = _header_functions("flce_probe.h")
-    assert declared == ["flce_probe_mfma_loop", "flce_probe_mfma_threads",
+    assert declared == ["flce_probe_mfma16_loop", "flce_probe_mfma_loop", "flce_probe_mfma_threads",
                         "flce_probe_read_stream", "flce_probe_stream_threads"]
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
                          check=True).stdout
@@ -55,15 +55,17 @@ def test_probe_library_exports_its_header(flce_lib):
     assert lib.flce_probe_mfma_threads() == 512
     assert lib.flce_probe_stream_threads() == 256
     # invalid arguments are refused before any launch
-    lib.flce_probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                         ctypes.c_void_p]
+    for f in (lib.flce_probe_mfma_loop, lib.flce_probe_mfma16_loop):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.flce_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     far = 1 << 44
-    assert lib.flce_probe_mfma_loop(far, 16, far, 511, 1, 1, None) == 1   # sink too small
-    assert lib.flce_probe_mfma_loop(far, 8, far, 512, 1, 1, None) == 1    # no whole fragment
-    assert lib.flce_probe_mfma_loop(None, 16, far, 512, 1, 1, None) == 1
+    for loop in (lib.flce_probe_mfma_loop, lib.flce_probe_mfma16_loop):
+        assert loop(far, 16, far, 511, 1, 1, None) == 1   # sink too small
+        assert loop(far, 8, far, 512, 1, 1, None) == 1    # no whole fragment
+        assert loop(None, 16, far, 512, 1, 1, None) == 1
+        assert loop(far, 16, far, 512, 1, -1, None) == 1  # negative iteration count
     assert lib.flce_probe_read_stream(far, 24, far, 4096, 1, None) == 1   # not a multiple of 16
     assert lib.flce_probe_read_stream(far, 32, far, 4095, 1, None) == 1   # sink too small
 

@@ -74,10 +74,19 @@ def test_extra_summaries():
 
 def test_ceiling_fraction_follows_the_bound():
     ceil = {"mfma_loop_bf16_random_tflops": 1600.0, "mfma_loop_bf16_zero_tflops": 2400.0,
+            "mfma16_loop_bf16_random_tflops": 2000.0, "mfma16_loop_bf16_zero_tflops": 2400.0,
             "hbm_read_stream_gbs": 6000.0, "hbm_copy_gbs": 5000.0}
     rl = dict(bound="mfma", achieved=800.0)
     bench.add_ceiling(rl, ceil, "bf16")
     assert rl["frac_of_ceiling"] == 0.5 and rl["ceiling"]["unit"] == "TFLOP/s"
+    # grad_input of large chunks runs on 16x16x32 MFMAs: that loop is its ceiling
+    for rows, frac in ((bench.DX_SUB16_ROWS, 0.4), (bench.DX_SUB16_ROWS - 1, 0.5)):
+        rl = dict(kernel="dx_gemm", bound="mfma", achieved=800.0, rows_per_launch=rows)
+        bench.add_ceiling(rl, ceil, "f16")
+        assert rl["frac_of_ceiling"] == frac
+    rl = dict(kernel="dw_gemm", bound="mfma", achieved=800.0, rows_per_launch=4096)
+    bench.add_ceiling(rl, ceil, "bf16")
+    assert rl["frac_of_ceiling"] == 0.5 and "32x32x16" in rl["ceiling"]["kind"]
     rl = dict(bound="hbm", achieved=4500.0)
     bench.add_ceiling(rl, ceil, "bf16")
     assert rl["frac_of_ceiling"] == 0.75 and rl["ceiling"]["unit"] == "GB/s"

@@ -3,8 +3,8 @@ claim, so that the ceilings `bench.py` reports measure real work.
 
 * the read stream visits every 16-byte element once: the XOR of all threads'
   sinks equals the XOR of the whole buffer (checked on the host);
-* the MFMA loop with all-zero operands leaves zero in every sink, and with
-  iters = 0 too; with random operands the sums are finite.
+* each MFMA loop (32x32x16 and 16x16x32) with all-zero operands leaves zero in
+  every sink, and with iters = 0 too; with random operands the sums are finite.
 """
 import ctypes
 import os
@@ -24,9 +24,9 @@ def probe():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     lib = ctypes.CDLL(os.path.join(PKG, "libflce_probe.so"))
-    lib.flce_probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                         ctypes.c_void_p]
+    for f in (lib.flce_probe_mfma_loop, lib.flce_probe_mfma16_loop):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.flce_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     return lib
@@ -50,25 +50,28 @@ def test_read_stream_visits_every_element(probe, nbytes, blocks):
     assert np.array_equal(got, want)
 
 
-def test_mfma_loop_zero_operands_and_no_iterations(probe):
+@pytest.mark.parametrize("loop_name", ["flce_probe_mfma_loop", "flce_probe_mfma16_loop"])
+def test_mfma_loop_zero_operands_and_no_iterations(probe, loop_name):
+    print(f"{loop_name}: 4 workgroups", flush=True)
+    loop = getattr(probe, loop_name)
     dev = torch.device("cuda:0")
     thr = probe.flce_probe_mfma_threads()
     blocks = 4
     st = torch.cuda.current_stream(dev).cuda_stream
     ops = torch.zeros(1 << 16, dtype=torch.bfloat16, device=dev)
     sink = torch.full((blocks * thr,), 7.0, device=dev)
-    assert probe.flce_probe_mfma_loop(ops.data_ptr(), ops.numel() * 2, sink.data_ptr(),
-                                      sink.numel(), blocks, 50, st) == 0
+    assert loop(ops.data_ptr(), ops.numel() * 2, sink.data_ptr(),
+                sink.numel(), blocks, 50, st) == 0
     torch.cuda.synchronize()
     assert torch.count_nonzero(sink).item() == 0
     rnd = (torch.randn(1 << 16, generator=torch.Generator().manual_seed(3)) * 0.05).to(
         torch.bfloat16).to(dev)
     sink.fill_(7.0)
-    assert probe.flce_probe_mfma_loop(rnd.data_ptr(), rnd.numel() * 2, sink.data_ptr(),
-                                      sink.numel(), blocks, 0, st) == 0
+    assert loop(rnd.data_ptr(), rnd.numel() * 2, sink.data_ptr(),
+                sink.numel(), blocks, 0, st) == 0
     torch.cuda.synchronize()
     assert torch.count_nonzero(sink).item() == 0
-    assert probe.flce_probe_mfma_loop(rnd.data_ptr(), rnd.numel() * 2, sink.data_ptr(),
-                                      sink.numel(), blocks, 20, st) == 0
+    assert loop(rnd.data_ptr(), rnd.numel() * 2, sink.data_ptr(),
+                sink.numel(), blocks, 20, st) == 0
     torch.cuda.synchronize()
     assert torch.isfinite(sink).all() and torch.count_nonzero(sink).item() > 0
