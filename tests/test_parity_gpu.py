@@ -227,6 +227,23 @@ def test_accumulate_on_every_grad_weight_tile(pkg, dtype, accum, chunk):
     _check(r, ref, dtype, "sum")
 
 
+@pytest.mark.parametrize("dtype,BT,chunk", [("bf16", 2047, 1024), ("f16", 2047, 1024),
+                                             ("bf16", 3073, 2048)])
+def test_grad_input_mfma_shape_boundary(pkg, dtype, BT, chunk):
+    """grad_input changes MFMA shape at 1024 rows per chunk (32x32x16 below,
+    16x16x32 from there).  Chunk sizes are powers of two, so the rows just
+    below and above the switch are ragged last chunks: 1024 + 1023 rows
+    (16x16 then 32x32) and 2048 + 1025 rows (both 16x16).  H = 392 and
+    V = 1100 are ragged against every tile."""
+    H, V = 392, 1100
+    X, W, t = si.make_case(BT, H, V, dtype, 2700 + BT + len(dtype), ignore="none", frac=0.0)
+    r = _run(pkg, X, W, t, reduction="mean", chunk_size=chunk, accum_dtype=torch.float32)
+    ref = oracle.flce(X, W, t, reduction="mean")
+    assert ref["n_valid"] == BT and r.stats["chunk_size"] == chunk
+    assert r.stats["chunks_run"] == 2
+    _check(r, ref, dtype, "mean")
+
+
 def test_frozen_weight(pkg):
     BT, H, V = 200, 128, 900
     X, W, t = si.make_case(BT, H, V, "bf16", 4003, ignore="prompt_first", frac=0.5, seq_len=100)
