@@ -53,9 +53,11 @@ __device__ __forceinline__ u16 f32_to_f16(float f) {
 // B[8 (l / 16) + 0..7][l % 16] and receives D[4 (l / 16) + e][l % 16],
 // e = 0..3; sub-block q = 2 (row half) + (column half) lives in accumulator
 // elements 4 q .. 4 q + 3.  Under this chip's power limit a loop of 16x16x32
-// MFMAs on random data sustains 1.98 PFLOP/s against 1.82 for 32x32x16 (2.44
-// and 2.43 with zero operands, where the clock stays at its maximum), but a
-// k-step needs twice the LDS reads of one operand per MFMA flop.
+// MFMAs on random data sustains 1.96-1.98 PFLOP/s against 1.68-1.82 for
+// 32x32x16 (2.44 and 2.43 with zero operands, where the clock stays at its
+// maximum).  The fragment bytes per flop are the same for both shapes, but a
+// k-step covers 32 k, so a k-tile holds half as many steps to hide each
+// step's reads behind.
 template <int Q, class V>
 __device__ __forceinline__ void mma16_sub(f32x16_t& c, V a, V b) {
   f32x4_t d = {c[4 * Q], c[4 * Q + 1], c[4 * Q + 2], c[4 * Q + 3]};
