@@ -415,7 +415,8 @@ __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned
     // ColSwz one) are read at its start: double buffering them across steps
     // needs twice the registers, and with the reads and MFMAs interleaved by
     // the same pinning as below it was 7 % slower (grad_input at chunk 2048,
-    // 1632 -> 1861 us per launch).
+    // 1632 -> 1861 us per launch); double buffering one operand and reading
+    // the other in halves, pinned, was 8 % slower (1622 -> 1750 us).
     u32x4_t fa[C::FM][2], fb[C::FN][2];
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
@@ -1282,10 +1283,11 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
 // the kernel is MFMA-bound.  Per launch, interleaved against 32x32x16 on the
 // Llama shape: chunk 256 258 -> 262 us, 512 and 1024 equal, 2048 1738 ->
 // 1691 us, 4096 3438 -> 3226 us; H 4096 / V 32000 with 16384 rows 451 ->
-// 425 us (bf16), 476 -> 433 us (fp16).  With few rows the kernel streams W
-// and the extra LDS reads of the 16x16 fragments cost more than they gain.
-// The logits and grad_weight GEMMs measured no gain (grad_weight at chunk
-// 2048 was 2 % slower) and keep 32x32x16.
+// 425 us (bf16), 476 -> 433 us (fp16).  With few rows the kernel streams W,
+// and the fragment-read latency that the 16x16 loop leaves exposed (two
+// k-steps per k-tile instead of four) costs more than the clock gains.  The
+// logits and grad_weight GEMMs measured no gain (grad_weight at chunk 2048
+// was 2 % slower) and keep 32x32x16.
 constexpr int kDxSub16Rows = 1024;
 template <class T>
 static hipError_t dx_t(const DxArgs& a, hipStream_t st) {
