@@ -386,6 +386,12 @@ __device__ __forceinline__ float frag4_of(const unsigned char* b, int blk, int s
 // before the MFMAs of step s, and the interleave is pinned for the
 // scheduler.  With 16x16x32 MFMAs (Mfma16) each step reads its own
 // fragments first.
+// Consecutive MFMAs share an operand fragment where they can: the blocks of
+// a wave row run in serpentine order, and 16x16 sub-blocks alternate their
+// order, so the multipliers' inputs change on one side only.  Under the
+// power limit that is worth a little clock: interleaved on MI355X, the Llama
+// shape at chunk 2048 23.21 -> 23.13 and 23.22 -> 23.11 ms per step, logits
+// and grad_input 0.5-1.6 % faster, grad_weight unchanged.
 // ---------------------------------------------------------------------------
 // Scheduling groups: NR LDS reads (mask 0x100) spread evenly between NM
 // MFMAs (mask 0x008), read q followed by its share of MFMAs.
@@ -431,11 +437,19 @@ __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          T::template mma16<0>(fa[i][0], fb[j][0], acc[i][j]);
-          T::template mma16<1>(fa[i][0], fb[j][1], acc[i][j]);
-          T::template mma16<2>(fa[i][1], fb[j][0], acc[i][j]);
-          T::template mma16<3>(fa[i][1], fb[j][1], acc[i][j]);
+        for (int jj = 0; jj < C::FN; ++jj) {
+          const int j = (i & 1) ? C::FN - 1 - jj : jj;
+          if (((i * C::FN + jj) & 1) == 0) {
+            T::template mma16<0>(fa[i][0], fb[j][0], acc[i][j]);
+            T::template mma16<1>(fa[i][0], fb[j][1], acc[i][j]);
+            T::template mma16<3>(fa[i][1], fb[j][1], acc[i][j]);
+            T::template mma16<2>(fa[i][1], fb[j][0], acc[i][j]);
+          } else {
+            T::template mma16<2>(fa[i][1], fb[j][0], acc[i][j]);
+            T::template mma16<3>(fa[i][1], fb[j][1], acc[i][j]);
+            T::template mma16<1>(fa[i][0], fb[j][1], acc[i][j]);
+            T::template mma16<0>(fa[i][0], fb[j][0], acc[i][j]);
+          }
         }
       dma(s);
     }
@@ -454,7 +468,10 @@ __device__ __forceinline__ void mma_tile(const unsigned char* Ab, const unsigned
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) T::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+        for (int jj = 0; jj < C::FN; ++jj) {
+          const int j = (i & 1) ? C::FN - 1 - jj : jj;
+          T::mma(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+        }
       dma(s);
     }
     // reads per step: one per RowSwz fragment, two per ColSwz fragment
