@@ -1292,19 +1292,28 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
   constexpr bool k16 = sizeof(typename T::storage) == 2;
   typedef typename std::conditional<k16, Big8M, Big>::type L;
   typedef typename std::conditional<k16, Small8, Small>::type LS;
+  if constexpr (k16)
+    if (a.sub16 && logits_shape(a.rows, a.V) == Shape::Big) return launch_logits_t<Mfma16<T>, L>(a, st);
   return logits_shape(a.rows, a.V) == Shape::Big ? launch_logits_t<T, L>(a, st)
                                                  : launch_logits_t<T, LS>(a, st);
 }
-// grad_input of chunks of at least kDxSub16Rows rows (16-bit operands) runs
-// on 16x16x32 MFMAs, which the power limit lets run at a higher clock where
-// the kernel is MFMA-bound.  Per launch, interleaved against 32x32x16 on the
-// Llama shape: chunk 256 258 -> 262 us, 512 and 1024 equal, 2048 1738 ->
-// 1691 us, 4096 3438 -> 3226 us; H 4096 / V 32000 with 16384 rows 451 ->
-// 425 us (bf16), 476 -> 433 us (fp16).  With few rows the kernel streams W,
-// and the fragment-read latency that the 16x16 loop leaves exposed (two
-// k-steps per k-tile instead of four) costs more than the clock gains.  The
-// logits and grad_weight GEMMs measured no gain (grad_weight at chunk 2048
-// was 2 % slower) and keep 32x32x16.
+// MFMA shape of the 16-bit GEMMs on the large tiles.  16x16x32 MFMAs draw
+// less power than 32x32x16 for the same flops, so under the chip's power
+// limit they run at a higher clock, but their loop leaves more fragment-read
+// latency exposed (two k-steps per k-tile instead of four).  Which wins
+// depends on the kernel and on what else the step runs (the clock follows
+// the power of the whole step).  Measured interleaved on MI355X:
+// - grad_input from kDxSub16Rows rows per chunk: Llama shape chunk 2048
+//   1738 -> 1691 us per launch, 4096 3438 -> 3226 us; H 4096 / V 32000 with
+//   16384 rows 451 -> 425 us (bf16), 476 -> 433 us (fp16); 512 and 1024 rows
+//   equal, 256 rows 258 -> 262 us (there the kernel streams W).
+// - logits, and grad_weight with a 16-bit dW, when the step does not
+//   accumulate an fp32 dW (LogitsArgs::sub16): steps 0.8-3.2 % faster (fp16
+//   sweep 11.65 -> 11.28 ms, bf16 sweep 11.28 -> 11.07 ms, H 5376 / V 262144
+//   with 32768 rows 247.8 -> 244.5 ms and at chunk 256 88.1 -> 86.7 ms, masked
+//   SFT at chunk 2048 14.27 -> 14.11 ms trained and 9.67 -> 9.59 ms frozen).
+//   With an fp32 dW, logits on 16x16 was 2.5-2.9 % slower per launch and the
+//   step unchanged, and grad_weight 2-3 % slower, so both keep 32x32x16.
 constexpr int kDxSub16Rows = 1024;
 template <class T>
 static hipError_t dx_t(const DxArgs& a, hipStream_t st) {
@@ -1326,6 +1335,7 @@ static hipError_t dw_t(const DwArgs& a, hipStream_t st) {
   if (dw_shape(a.rows, a.H, k16) != Shape::Big) return launch_dw_t<T, Small, D>(a, st);
   if constexpr (k16)
     if (a.rows <= 128) return launch_dw_t<T, Twin8M, D>(a, st);
+  if constexpr (k16 && !std::is_same<D, float>::value) return launch_dw_t<Mfma16<T>, L, D>(a, st);
   return launch_dw_t<T, L, D>(a, st);
 }
 
