@@ -559,9 +559,6 @@ int fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, in
     la.bias = o.bias;
     la.amax = amax;
     la.store_slab = grads ? 1 : 0;
-    // logits on 16x16x32 MFMAs unless the step accumulates an fp32 dW (the
-    // GEMM kernels state the measurements)
-    la.sub16 = (want_dw && dw_dt == FLCE_F32) ? 0 : 1;
     if (!L.x_gather) {
       FLCE_LAUNCH(FLCE_K_LOGITS, launch_logits(dt, la, st));
     } else {

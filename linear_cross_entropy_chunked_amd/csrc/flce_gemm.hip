@@ -1293,7 +1293,7 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
   typedef typename std::conditional<k16, Big8M, Big>::type L;
   typedef typename std::conditional<k16, Small8, Small>::type LS;
   if constexpr (k16)
-    if (a.sub16 && logits_shape(a.rows, a.V) == Shape::Big) return launch_logits_t<Mfma16<T>, L>(a, st);
+    if (logits_shape(a.rows, a.V) == Shape::Big) return launch_logits_t<Mfma16<T>, L>(a, st);
   return logits_shape(a.rows, a.V) == Shape::Big ? launch_logits_t<T, L>(a, st)
                                                  : launch_logits_t<T, LS>(a, st);
 }
@@ -1307,13 +1307,16 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
 //   1738 -> 1691 us per launch, 4096 3438 -> 3226 us; H 4096 / V 32000 with
 //   16384 rows 451 -> 425 us (bf16), 476 -> 433 us (fp16); 512 and 1024 rows
 //   equal, 256 rows 258 -> 262 us (there the kernel streams W).
-// - logits, and grad_weight with a 16-bit dW, when the step does not
-//   accumulate an fp32 dW (LogitsArgs::sub16): steps 0.8-3.2 % faster (fp16
-//   sweep 11.65 -> 11.28 ms, bf16 sweep 11.28 -> 11.07 ms, H 5376 / V 262144
-//   with 32768 rows 247.8 -> 244.5 ms and at chunk 256 88.1 -> 86.7 ms, masked
-//   SFT at chunk 2048 14.27 -> 14.11 ms trained and 9.67 -> 9.59 ms frozen).
-//   With an fp32 dW, logits on 16x16 was 2.5-2.9 % slower per launch and the
-//   step unchanged, and grad_weight 2-3 % slower, so both keep 32x32x16.
+// - logits and grad_weight on the large tiles, with the MFMA order that
+//   shares operands (mma_tile): with a 16-bit dW or none, steps 0.8-3.2 %
+//   faster (fp16 sweep 11.65 -> 11.28 ms, bf16 sweep 11.28 -> 11.07 ms,
+//   H 5376 / V 262144 with 32768 rows 247.8 -> 244.5 ms and at chunk 256
+//   88.1 -> 86.7 ms, masked SFT at chunk 2048 14.27 -> 14.11 ms trained and
+//   9.67 -> 9.59 ms frozen).  With an fp32 dW grad_weight is 3.5 % slower per
+//   launch on 16x16x32, but it then leaves logits and grad_input more of the
+//   power budget: the Llama shape at chunk 2048 23.03 -> 22.85 and 23.16 ->
+//   22.94 ms per step (logits -4 %, grad_input -3.7 %), chunks 256 and 4096
+//   0.1 % faster.
 constexpr int kDxSub16Rows = 1024;
 template <class T>
 static hipError_t dx_t(const DxArgs& a, hipStream_t st) {
@@ -1335,7 +1338,7 @@ static hipError_t dw_t(const DwArgs& a, hipStream_t st) {
   if (dw_shape(a.rows, a.H, k16) != Shape::Big) return launch_dw_t<T, Small, D>(a, st);
   if constexpr (k16)
     if (a.rows <= 128) return launch_dw_t<T, Twin8M, D>(a, st);
-  if constexpr (k16 && !std::is_same<D, float>::value) return launch_dw_t<Mfma16<T>, L, D>(a, st);
+  if constexpr (k16) return launch_dw_t<Mfma16<T>, L, D>(a, st);
   return launch_dw_t<T, L, D>(a, st);
 }
 

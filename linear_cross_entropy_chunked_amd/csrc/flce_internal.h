@@ -22,7 +22,6 @@ struct LogitsArgs {
   const void* bias;        // [V] operand dtype, added to every row's logits; NULL = none
   int32_t* amax;           // [rows_cap, stats_ld] column of each block's maximum; NULL = not needed
   int store_slab;          // 0: logits are not stored (loss-only call)
-  int sub16;               // 1: the large 16-bit tile runs on 16x16x32 MFMAs
 };
 
 // Softmax-gradient pass of one chunk.
