@@ -470,19 +470,32 @@ def ceilings(dev):
     return out
 
 
-# 16-bit grad_input launches of at least this many rows run on 16x16x32 MFMAs
-# (kDxSub16Rows in flce_gemm.hip); every other 16-bit GEMM on 32x32x16.
+# Which 16-bit GEMM launches run on 16x16x32 MFMAs (flce_gemm.hip): grad_input
+# from DX_SUB16_ROWS rows per chunk; logits and grad_weight on their large tiles,
+# i.e. more than LARGE_TILE_ROWS rows per chunk (logits also needs V >= 1024,
+# grad_weight H >= 256).  Everything else runs on 32x32x16.
 DX_SUB16_ROWS = 1024
+LARGE_TILE_ROWS = 128
 
 
-def add_ceiling(rl, ceil, dtype):
+def runs_sub16(kernel, rows, H=None, V=None):
+    if kernel == "dx_gemm":
+        return rows >= DX_SUB16_ROWS
+    if kernel == "logits_gemm":
+        return rows > LARGE_TILE_ROWS and (V is None or V >= 1024)
+    if kernel == "dw_gemm":
+        return rows > LARGE_TILE_ROWS and (H is None or H >= 256)
+    return False
+
+
+def add_ceiling(rl, ceil, dtype, H=None, V=None):
     """The dominant kernel's rate against what the chip sustains by itself: the
     MFMA loop of the shape the kernel runs on (chosen by the average rows per
     launch), or the HBM read stream."""
     if not ceil:
         return
     if rl["bound"] == "mfma" and dtype in ("bf16", "f16"):
-        sub16 = rl.get("kernel") == "dx_gemm" and rl.get("rows_per_launch", 0) >= DX_SUB16_ROWS
+        sub16 = runs_sub16(rl.get("kernel"), rl.get("rows_per_launch", 0), H, V)
         key, shape = ("mfma16_loop", "16x16x32") if sub16 else ("mfma_loop", "32x32x16")
         c = ceil[f"{key}_bf16_random_tflops"]
         rl["ceiling"] = dict(value=c, unit="TFLOP/s", kind=f"bf16 {shape} MFMA loop, random operands")
@@ -1017,7 +1030,8 @@ def main():
         log("ceilings: MFMA loop (random, zero operands), HBM read stream, device copy")
         ceil = ceilings(dev)
         for name, res in extras.items():
-            add_ceiling(res["roofline"], ceil, WORKLOADS[name]["dtype"])
+            add_ceiling(res["roofline"], ceil, WORKLOADS[name]["dtype"], WORKLOADS[name]["H"],
+                        WORKLOADS[name]["V"])
     rl = roofline(main_res, cfg)
     rl["traffic"] = recorded_traffic(rl["kernel"], a.workload)
     sens = main_res["gpu_sensors"]
@@ -1028,7 +1042,7 @@ def main():
         if mhz:
             rl["frac_at_measured_clock"] = rl["frac"] * 2400.0 / mhz
             rl["measured_clock_mhz"] = mhz
-    add_ceiling(rl, ceil, cfg["dtype"])
+    add_ceiling(rl, ceil, cfg["dtype"], cfg["H"], cfg["V"])
     out = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],

@@ -84,9 +84,17 @@ def test_ceiling_fraction_follows_the_bound():
         rl = dict(kernel="dx_gemm", bound="mfma", achieved=800.0, rows_per_launch=rows)
         bench.add_ceiling(rl, ceil, "f16")
         assert rl["frac_of_ceiling"] == frac
-    rl = dict(kernel="dw_gemm", bound="mfma", achieved=800.0, rows_per_launch=4096)
+    # logits and grad_weight on their large tiles (more than 128 rows) run on 16x16x32
+    for kern in ("dw_gemm", "logits_gemm"):
+        rl = dict(kernel=kern, bound="mfma", achieved=800.0, rows_per_launch=2048)
+        bench.add_ceiling(rl, ceil, "bf16", 4096, 128256)
+        assert rl["frac_of_ceiling"] == 0.4 and "16x16x32" in rl["ceiling"]["kind"]
+        rl = dict(kernel=kern, bound="mfma", achieved=800.0, rows_per_launch=128)
+        bench.add_ceiling(rl, ceil, "bf16", 4096, 128256)
+        assert rl["frac_of_ceiling"] == 0.5 and "32x32x16" in rl["ceiling"]["kind"]
+    rl = dict(kernel="softmax_grad", bound="mfma", achieved=800.0, rows_per_launch=2048)
     bench.add_ceiling(rl, ceil, "bf16")
-    assert rl["frac_of_ceiling"] == 0.5 and "32x32x16" in rl["ceiling"]["kind"]
+    assert rl["frac_of_ceiling"] == 0.5
     rl = dict(bound="hbm", achieved=4500.0)
     bench.add_ceiling(rl, ceil, "bf16")
     assert rl["frac_of_ceiling"] == 0.75 and rl["ceiling"]["unit"] == "GB/s"
