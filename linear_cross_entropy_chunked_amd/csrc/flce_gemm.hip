@@ -1317,6 +1317,8 @@ static hipError_t logits_t(const LogitsArgs& a, hipStream_t st) {
 //   power budget: the Llama shape at chunk 2048 23.03 -> 22.85 and 23.16 ->
 //   22.94 ms per step (logits -4 %, grad_input -3.7 %), chunks 256 and 4096
 //   0.1 % faster.
+// - the small tiles (chunks of at most 128 rows) keep 32x32x16: those chunks
+//   stream W from HBM, and 16x16x32 there was 0.2-0.3 % slower.
 constexpr int kDxSub16Rows = 1024;
 template <class T>
 static hipError_t dx_t(const DxArgs& a, hipStream_t st) {
